@@ -1,0 +1,8 @@
+"""CPU oracle (float64) for the BailingMoeV3 sparse MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  The HIP library never calls it and shares no code
+with it.
+"""
+from .moe_oracle import (Dispatch, Routing, bf16_to_f64, dispatch, expert_forward,  # noqa: F401
+                         expert_hidden, moe_layer, mxfp4_dequant, route, router_logits, swiglu)
