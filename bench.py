@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of one BailingMoeV3 sparse MoE layer forward (hidden 2560, 512 routed experts of
+intermediate 768 in 8 groups, top-4 groups, top-8, one shared expert) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|mxfp4]
+
+A step is one moe_forward call (router, dispatch, expert FFNs, combine) over one batch of
+seeded synthetic tokens already resident in HBM.  Prints one JSON line with tokens/s, the
+roofline of the dominant kernel (timed live with HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.  The secondary object `prefill` holds
+the T=8192 measurement the headline metric also names.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------------
+# HIP events on the library's stream (torch's events only see torch's current stream)
+# ----------------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        for n in ("hipEventCreate", "hipEventDestroy", "hipEventSynchronize", "hipEventElapsedTime",
+                  "hipEventRecord"):
+            getattr(self.lib, n).restype = ctypes.c_int
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+
+# ----------------------------------------------------------------------------------
+# workload
+# ----------------------------------------------------------------------------------
+def upload(shape, experts, seed=0):
+    import torch
+    from synthetic import gen_bias, gen_router, gen_shared, gen_x
+    import sparse_moe_layer_bailingmoev3_amd as moe
+
+    def dev(a, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if bf16 else np.ascontiguousarray(a))
+        t = t.cuda()
+        return t.view(torch.bfloat16) if bf16 else t
+
+    x_bits = gen_x(shape, seed)
+    d = dict(x_bits=x_bits, x=dev(x_bits, True), router_w_np=gen_router(shape, seed), bias_np=gen_bias(shape, seed))
+    d["router_w"], d["bias"] = dev(d["router_w_np"]), dev(d["bias_np"])
+    sh = gen_shared(shape, seed)
+    d["shared_np"] = sh
+    shared = [dev(sh[k], True) for k in ("gate", "up", "down")]
+    if shape.weight_format == "mxfp4":
+        w = moe.MoEExpertWeights(*[dev(experts[k]) for k in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")],
+                                 *shared)
+    else:
+        w = moe.MoEExpertWeights(*[dev(experts[k], True) for k in ("gate", "up", "down")],
+                                 shared_gate=shared[0], shared_up=shared[1], shared_down=shared[2])
+    d["weights"] = w
+    return d
+
+
+def cfg_for(shape):
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    return moe.MoEConfig(hidden_size=shape.H, num_experts=shape.E, num_experts_per_tok=shape.K, n_group=shape.G,
+                         topk_group=shape.TG, moe_intermediate_size=shape.I,
+                         num_shared_experts=shape.num_shared_experts, shared_intermediate_size=shape.I_s,
+                         norm_topk_prob=int(shape.norm_topk_prob), routed_scaling_factor=shape.routed_scaling_factor,
+                         swiglu_limit=shape.swiglu_limit, shared_swiglu_limit=shape.shared_swiglu_limit,
+                         expert_weight_format=moe.MOE_WEIGHTS_MXFP4 if shape.weight_format == "mxfp4"
+                         else moe.MOE_WEIGHTS_BF16)
+
+
+def expert_bytes(shape):
+    """Bytes of one routed expert's weights (gate, up, down) in its storage format."""
+    n = 3 * shape.H * shape.I
+    return n // 2 + n // 32 if shape.weight_format == "mxfp4" else 2 * n
+
+
+def measure(shape, d, steps, warmup, hip):
+    """Time `steps` forwards; returns dict with ms/step and per-kernel mean durations."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    cfg = cfg_for(shape)
+    T = shape.T
+    ws = torch.empty(moe.moe_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, shape.H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, shape.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shape.K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((shape.E + 1,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
+    torch.cuda.synchronize()
+
+    # timed region: `steps` traced forwards; events between kernels cost no GPU work
+    nev = 24
+    events = [[hip.event() for _ in range(nev)] for _ in range(steps)]
+    t_start, t_end = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(t_start, stream)
+    names = None
+    for s in range(steps):
+        names = moe.moe_forward_traced(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, events[s])
+    hip.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = hip.elapsed_ms(t_start, t_end) / steps
+    per_kernel = {}
+    for s in range(steps):
+        for i, n in enumerate(names):
+            per_kernel.setdefault(n, []).append(hip.elapsed_ms(events[s][i], events[s][i + 1]))
+    kmean = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    # routing of the last step (for algorithmic bytes)
+    moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
+    torch.cuda.synchronize()
+    counts = cnt.cpu().numpy()
+    return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, counts=counts, out=out)
+
+
+def roofline(shape, r):
+    """Roofline of the dominant kernel (the longest of the step).
+
+    Algorithmic bytes per launch (what the method has to move, once):
+      expert_gate_up: (touched routed experts + shared) * 2*I*H weights in their storage
+                      format + x [T,H] bf16 read + h [T*K + T, I] bf16 written;
+      expert_down:    (touched + shared) * H*I weights + h read + y [T*K + T, H] fp32 written.
+    bf16 FLOPs per launch: 4*H*I per (token, expert) pair for gate/up, 2*H*I for down."""
+    counts = r["counts"]
+    E, H, I, K, T = shape.E, shape.H, shape.I, shape.K, shape.T
+    touched = int((counts[:E] > 0).sum())
+    S = shape.num_shared_experts
+    pairs = T * K + T * S
+    eb = expert_bytes(shape)
+    per_mat = eb // 3
+    sh_mat = 2 * H * I  # shared expert is bf16
+    ks = r["kernels"]
+    dom = max(("expert_gate_up", "expert_down"), key=lambda n: ks.get(n, 0.0))
+    if dom == "expert_gate_up":
+        byts = touched * 2 * per_mat + S * 2 * sh_mat + T * H * 2 + pairs * I * 2
+        flops = 4.0 * H * I * pairs
+    else:
+        byts = touched * per_mat + S * sh_mat + pairs * I * 2 + pairs * H * 4
+        flops = 2.0 * H * I * pairs
+    ms = ks[dom]
+    gbs = byts / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    hbm_time = byts / (HBM_PEAK_GBS * 1e9)
+    mfma_time = flops / (BF16_PEAK_TFLOPS * 1e12)
+    if hbm_time >= mfma_time:
+        rl = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        rl = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                  frac=round(tflops / BF16_PEAK_TFLOPS, 4))
+    rl.update(kernel=dom, kernel_ms=round(ms, 4), algorithmic_bytes=int(byts), bf16_flops=flops,
+              touched_experts=touched, traffic=None)
+    return rl
+
+
+def layer_summary(shape, r):
+    """Whole-layer figures: algorithmic bytes of the step and fractions of both peaks."""
+    counts = r["counts"]
+    E, H, I, K, T = shape.E, shape.H, shape.I, shape.K, shape.T
+    touched = int((counts[:E] > 0).sum())
+    S = shape.num_shared_experts
+    byts = touched * expert_bytes(shape) + S * 3 * H * I * 2 + E * H * 4 + E * 4 + 2 * T * H * 2
+    flops = 6.0 * H * I * (T * K + T * S)
+    ms = r["wall_ms"]
+    return dict(algorithmic_bytes=int(byts), hbm_frac=round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                bf16_flops=flops, mfma_frac=round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                router_fp32_flops=2.0 * T * H * E, touched_experts=touched)
+
+
+def cpu_baseline(shape, d, experts, max_tokens):
+    """The float64 oracle on the host cores, on the first `max_tokens` tokens of the workload."""
+    import oracle
+    T = min(shape.T, max_tokens)
+    x = oracle.bf16_to_f64(d["x_bits"][:T])
+
+    def get(e):
+        if shape.weight_format == "mxfp4":
+            return tuple(oracle.mxfp4_dequant(experts[k + "_q"][e], experts[k + "_s"][e]) for k in ("gate", "up", "down"))
+        return tuple(oracle.bf16_to_f64(experts[k][e]) for k in ("gate", "up", "down"))
+    sh = tuple(oracle.bf16_to_f64(d["shared_np"][k]) for k in ("gate", "up", "down"))
+    t0 = time.perf_counter()
+    oracle.moe_layer(x, d["router_w_np"], d["bias_np"], get, sh, n_group=shape.G, topk_group=shape.TG,
+                     top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
+                     norm_topk_prob=shape.norm_topk_prob, swiglu_limit=shape.swiglu_limit,
+                     shared_swiglu_limit=shape.shared_swiglu_limit)
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return dict(value=round(T / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"float64 oracle forward of the first {T} tokens of the {shape.name} workload "
+                       f"(H{shape.H}/E{shape.E}/top{shape.K}), {dt:.1f} s")
+
+
+def copy_probe(hip, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: {nbytes} bytes read and written per copy")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this layer is built and timed on a single MI355X, "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synthetic import CONFIGS, gen_experts
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    moe.load_library()  # no fallback: fails loudly without the HIP library
+    assert torch.cuda.is_available(), "no GPU visible"
+    hip = Hip()
+
+    if args.copy_probe:
+        copy_probe(hip)
+
+    shape = CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    base = CONFIGS["decode"] if shape.weight_format != "mxfp4" else shape
+    log(f"drawing {shape.E} experts ({shape.weight_format}) ...")
+    experts = gen_experts(base if shape.weight_format != "mxfp4" else shape, seed=0)
+    log(f"  {time.perf_counter() - t0:.1f} s; uploading")
+    d = upload(shape, experts)
+    torch.cuda.synchronize()
+    log(f"measuring {shape.name} T={shape.T}: warmup {args.warmup}, steps {args.steps}")
+    r = measure(shape, d, args.steps, args.warmup, hip)
+    ms = r["wall_ms"]
+    line = {
+        "metric": "MoE-layer tokens/s, H2560/E512/top8, T=64 & T=8192; % of HBM or MFMA peak",
+        "value": round(shape.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.weight_format == "bf16" else "mxfp4-w/bf16",
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": f"{shape.name}: T={shape.T}, hidden {shape.H}, {shape.E} experts (I={shape.I}) "
+                               f"in {shape.G} groups, top-{shape.TG} groups, top-{shape.K}, 1 shared expert",
+                   "T": shape.T, "hidden_size": shape.H, "num_experts": shape.E, "moe_intermediate_size": shape.I,
+                   "n_group": shape.G, "topk_group": shape.TG, "num_experts_per_tok": shape.K,
+                   "weights": shape.weight_format, "parallelism": "single GPU"},
+        "roofline": roofline(shape, r),
+        "layer": layer_summary(shape, r),
+        "kernels_ms": {k: round(v, 4) for k, v in r["kernels"].items()},
+        "event_ms_per_step": round(r["event_ms"], 4),
+    }
+    if not args.no_prefill and shape.name == "decode":
+        p = CONFIGS["prefill"]
+        dp = upload(p, experts)
+        log(f"measuring prefill T={p.T}")
+        rp = measure(p, dp, max(5, args.steps // 3), 3, hip)
+        line["prefill"] = {"workload": f"prefill: T={p.T}, same layer", "value": round(p.T / (rp["wall_ms"] * 1e-3), 1),
+                           "unit": "tokens/s", "ms_per_step": round(rp["wall_ms"], 4), "roofline": roofline(p, rp),
+                           "layer": layer_summary(p, rp), "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
+        del dp
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(shape, d, experts, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

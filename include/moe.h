@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of one BailingMoeV3 sparse MoE layer
+ * (Ling-3.0-flash / Ling-3.0-flash-VL) on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (Ling-3.0-flash-VL routing walk-through page, lqnn.cn,
+ * "MoE 稀疏路由机制"):
+ *   section 三.1  router: one raw score per routed expert from the hidden state, then
+ *                 an element-wise sigmoid (score_function "sigmoid");
+ *   section 三.3  a per-expert bias is added to the score used for selection
+ *                 (moe_router_enable_expert_bias);
+ *   section 三.2  the experts form n_group equal groups; keep the topk_group groups
+ *                 with the largest in-group maximum, then the num_experts_per_tok best
+ *                 experts inside the kept groups;
+ *   section 四    router in fp32 (router_dtype), weights renormalised to sum to 1
+ *                 (norm_topk_prob) and multiplied by routed_scaling_factor; SwiGLU
+ *                 activations optionally clamped (expert_swiglu_limit_list);
+ *   section 二    each expert is a SwiGLU FFN (gate, up: hidden -> intermediate;
+ *                 down: intermediate -> hidden) and one shared expert sees every token.
+ * Routed-expert weights may be MXFP4 (hybrid-attention page, lpnh.cn, table 模型一览).
+ * The block is BailingMoeV3SparseMoeBlock (Ling-3.0-flash page, wmrh.cn, section
+ * 稀疏MoE设计).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device pointers the caller owns; the library
+ *     keeps no pointer and no state after a call returns and allocates nothing.
+ *     Every device pointer must be 16-byte aligned.  Outputs must not alias inputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *     only enqueue work: they return before the GPU finishes, and a fault inside a
+ *     kernel surfaces at the caller's next synchronisation as a HIP error.
+ *   - Argument errors are found on the host before anything is enqueued and return a
+ *     negative status; moe_last_error() then describes the failure (thread-local).
+ *   - T (tokens) may be 0: the call returns MOE_OK and enqueues nothing.
+ *   - Matrices are row-major.  bf16 tensors are passed as raw 16-bit patterns.
+ *   - Results are bitwise reproducible run to run: no reduction uses atomics.
+ *
+ * Shapes (T tokens; symbols used below)
+ *   H = hidden_size, E = num_experts, K = num_experts_per_tok, I = moe_intermediate_size,
+ *   S = num_shared_experts (0 or 1), P = T*K + T*S sorted positions.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, flag or pointer is out of range or NULL */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid configuration these kernels do not implement */
+  MOE_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -5          /* a HIP launch failed; moe_last_error() has the HIP text */
+} moe_status_t;
+
+typedef enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_MXFP4 = 1 } moe_weight_format_t;
+
+/* Layer configuration.  Field names follow the model's config.json text_config as the
+ * routing walk-through page quotes them (sections 二, 三.2 and 四). */
+typedef struct {
+  int32_t hidden_size;              /* H; multiple of 128 */
+  int32_t num_experts;              /* E routed experts; multiple of 64, at most 1024 */
+  int32_t num_experts_per_tok;      /* K, 1..16 and at most topk_group*E/n_group */
+  int32_t n_group;                  /* groups; divides 64 and E */
+  int32_t topk_group;               /* kept groups, 1..n_group */
+  int32_t moe_intermediate_size;    /* I; multiple of 128 */
+  int32_t num_shared_experts;       /* S: 0 or 1 */
+  int32_t shared_intermediate_size; /* must equal I when S == 1 */
+  int32_t norm_topk_prob;           /* nonzero: renormalise the K weights to sum to 1 */
+  float routed_scaling_factor;      /* multiplies the routed weights (2.5) */
+  float swiglu_limit;               /* > 0: clamp routed activations to [-limit, limit] */
+  float shared_swiglu_limit;        /* > 0: clamp shared-expert activations */
+  int32_t expert_weight_format;     /* moe_weight_format_t of the routed experts */
+} moe_config_t;
+
+/* Expert weights, all device pointers, PyTorch [out_features, in_features] layout.
+ *   MOE_WEIGHTS_BF16:  gate [E,I,H], up [E,I,H], down [E,H,I] bf16; *_scale NULL.
+ *   MOE_WEIGHTS_MXFP4: gate [E,I,H/2], up [E,I,H/2], down [E,H,I/2] uint8, two e2m1
+ *                      codes per byte (low nibble = even k, nibble = sign<<3 | code),
+ *                      gate_scale/up_scale [E,I,H/32], down_scale [E,H,I/32] e8m0
+ *                      bytes (value = e2m1 * 2^(scale-127), one scale per 32 k).
+ *   Shared expert (bf16, required when S == 1, else ignored):
+ *                      shared_gate [I,H], shared_up [I,H], shared_down [H,I]. */
+typedef struct {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const uint8_t* gate_scale;
+  const uint8_t* up_scale;
+  const uint8_t* down_scale;
+  const void* shared_gate;
+  const void* shared_up;
+  const void* shared_down;
+} moe_expert_weights_t;
+
+/* Bytes of device workspace that any entry point needs for T tokens (host call). */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes);
+
+/* Router (sections 三.1-三.3 and 四 of the routing walk-through page).
+ *   x           device bf16 [T,H]   hidden states
+ *   router_w    device fp32 [E,H]   router weight
+ *   expert_bias device fp32 [E]     selection bias; NULL means no bias
+ *   topk_idx    device int32 [T,K]  chosen experts of each token, ascending id
+ *   topk_w      device fp32 [T,K]   their mixing weights, same order
+ *   ws          device workspace of at least moe_workspace_size() bytes
+ * Logits are computed in fp32 (bf16 x times fp32 W_r, fp32 accumulation); sigmoid,
+ * bias, group scores and the selection are fp32.  Exact ties go to the lower group or
+ * expert index.  The weight of a chosen expert is its unbiased sigmoid score. */
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                       const float* expert_bias, int32_t* topk_idx, float* topk_w, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Dispatch: group the T*K (token, slot) pairs by expert.
+ *   topk_idx       device int32 [T,K] (each token's K ids distinct and in [0,E);
+ *                  out-of-range ids are ignored and their slot gets inv_perm = -1)
+ *   expert_counts  device int32 [E+1] tokens per expert; entry E = shared expert (T*S)
+ *   expert_offsets device int32 [E+2] exclusive prefix sum of expert_counts
+ *   sorted_token   device int32 [P]   positions offsets[e]..offsets[e+1]-1 hold the
+ *                  tokens of expert e in ascending order; the shared expert's block
+ *                  holds 0..T-1
+ *   inv_perm       device int32 [T,K] sorted position of each (token, slot) */
+moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx,
+                          int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,
+                          int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs (section 二 and 四): for every sorted position p of expert e and token
+ * t = sorted_token[p],  y_sorted[p] = down_e( clamp( silu(gate_e x_t) * up_e x_t ) ).
+ *   x              device bf16 [T,H]
+ *   expert_offsets device int32 [E+2], sorted_token device int32 [P] (from moe_dispatch)
+ *   weights        host pointer to the device weight table above
+ *   y_sorted       device fp32 [P,H]  (rows of the shared expert at T*K + t)
+ * gate/up and down run on bf16 MFMA with fp32 accumulation.  The activation between them
+ * is kept as two bf16 planes (hi = bf16(a), lo = bf16(a - hi)) and the down projection
+ * multiplies both, so it keeps about 16 significand bits; MXFP4 weights are decoded
+ * exactly to bf16 in registers. */
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
+                            const int32_t* expert_offsets, const int32_t* sorted_token,
+                            const moe_expert_weights_t* weights, void* y_sorted, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Combine: out[t] = sum_k topk_w[t,k] * y_sorted[inv_perm[t,k]]  (k ascending, fp32)
+ *                   + y_sorted[T*K + t] when S == 1,   rounded once to bf16.
+ *   y_sorted device fp32 [P,H], inv_perm device int32 [T,K], topk_w device fp32 [T,K],
+ *   out device bf16 [T,H].  Slots with inv_perm < 0 contribute nothing. */
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_sorted,
+                         const int32_t* inv_perm, const float* topk_w, void* out, void* stream);
+
+/* The whole layer: route, dispatch, expert FFNs, combine.
+ *   out                device bf16 [T,H]
+ *   topk_idx_out, topk_w_out, expert_counts_out: optional device copies of the
+ *   routing ([T,K] int32, [T,K] fp32, [E+1] int32); NULL to skip.
+ * Equivalent to the four calls above in order, with the same results bit for bit. */
+moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                         const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                         int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with a timing trace, for profiling (same results).  events[0] is recorded on
+ * `stream` before the first kernel and events[i+1] right after the i-th kernel launch; the
+ * caller creates the events (hipEvent_t, passed as void*) and later reads the elapsed times.
+ * kernel_names (host array of max_events - 1 pointers) receives static kernel names and
+ * *n_kernels the number of kernels launched.  Returns MOE_ERR_INVALID_ARG (after running
+ * the layer) if max_events is smaller than n_kernels + 1. */
+moe_status_t moe_forward_traced(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                                void* ws, size_t ws_bytes, void* stream, void* const* events,
+                                int32_t max_events, const char** kernel_names, int32_t* n_kernels);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Description of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,401 @@
+// Expert FFNs of the BailingMoeV3 sparse MoE block as a grouped GEMM on bf16 MFMA.
+//
+// Each expert is a SwiGLU FFN of three matrices, gate and up (hidden -> intermediate) and
+// down (intermediate -> hidden) (Ling-3.0-flash-VL routing walk-through page, lqnn.cn,
+// section 二); activations may be clamped to +-limit (section 四, expert_swiglu_limit_list);
+// routed-expert weights may be MXFP4 (hybrid-attention page, lpnh.cn, table 模型一览).
+//
+// Work unit (one workgroup): expert e, a tile of up to 16*MF consecutive sorted positions
+// of that expert, and a block of NW*RF*16 weight rows.  Design for gfx950:
+//   * weights are the MFMA a operand and stream from HBM straight into registers, each
+//     wave owning RF 16-row blocks (no LDS round trip, every weight byte is read by exactly
+//     one wave); two steps of loads are kept in flight;
+//   * the token rows (gathered x rows for gate/up, contiguous h rows for down) are the b
+//     operand, staged once per workgroup in double-buffered LDS and shared by all waves;
+//   * the reduction dimension is consumed KS values per step; lane group q of a 16-row
+//     operand owns the contiguous slice [q*KS/4, (q+1)*KS/4) of the step and MFMA sub-step s
+//     takes its s-th 8-value piece (the same permutation of k for both operands, so the
+//     dot products are unchanged and every lane loads one contiguous run);
+//   * gate and up share the token operand; SwiGLU and the clamp run on the accumulators;
+//     the activation h is stored as two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
+//     and the down projection runs one MFMA per plane, so h keeps ~16 significand bits
+//     through the down GEMM; the down projection writes fp32 expert outputs;
+//   * MXFP4 weights (KS = 128: one 16-byte load = 32 codes = one scale block per lane) are
+//     decoded exactly to bf16 in registers;
+//   * the work list (tiles per expert) lives on the device; consecutive work ids are placed
+//     on the same XCD so the row blocks of one tile share its token rows in that XCD's L2.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int MODE_GATEUP = 0, MODE_DOWN = 1;
+
+struct FfnArgs {
+  const uint16_t* act;          // gate/up: x [T,K]; down: h hi plane [P,K]
+  const uint16_t* act_lo;       // down: h lo plane [P,K]
+  const int32_t* sorted_token;  // gate/up: token of each sorted position
+  const int32_t* offsets;       // [E+2]
+  const int32_t* tile_prefix;   // [E+2] tiles of all experts before e
+  const void* w0;               // routed gate (gate/up) or down
+  const void* w1;               // routed up (gate/up)
+  const uint8_t* s0;            // MXFP4 scales of w0
+  const uint8_t* s1;            // MXFP4 scales of w1
+  const void* sw0;              // shared expert gate or down
+  const void* sw1;              // shared expert up
+  void* out;                    // gate/up: h hi plane bf16 [P,N]; down: y fp32 [P,N]
+  uint16_t* out_lo;             // gate/up: h lo plane bf16 [P,N]
+  int T, E, S;
+  int K;                        // reduction length
+  int N;                        // output columns per expert
+  int nrb;                      // row blocks per expert (N / rows per workgroup)
+  float limit, shared_limit;
+};
+
+__device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// e2m1 code (sign<<3 | magnitude code) times a power of two, as an fp32 bit pattern.
+// Magnitudes: code 0 -> 0, 1 -> 0.5, c >= 2 -> (1 + (c&1)/2) * 2^((c>>1) - 1).
+__device__ __forceinline__ uint32_t e2m1_scaled_bits(uint32_t nib, float scale) {
+  const uint32_t c = nib & 7u;
+  uint32_t mag = (c < 2u) ? (c ? 0x3F000000u : 0u) : ((((c >> 1) + 126u) << 23) | ((c & 1u) << 22));
+  float v = __uint_as_float(mag) * scale;  // exact: at most two significant bits
+  return __float_as_uint(v) | ((nib & 8u) << 28);
+}
+
+// 8 codes (low nibble first) -> 8 bf16 (exact, so truncation is the conversion)
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t v, float scale) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t b0 = e2m1_scaled_bits((v >> (8 * i)) & 0xFu, scale);
+    uint32_t b1 = e2m1_scaled_bits((v >> (8 * i + 4)) & 0xFu, scale);
+    o[i] = (b0 >> 16) | (b1 & 0xFFFF0000u);
+  }
+  return o;
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);  // 2^(s-127)
+}
+
+template <int NMAT, int RF, int WREGS>
+struct WStage {
+  u32x4 w[NMAT][RF][WREGS];
+  uint32_t sc[NMAT][RF];
+};
+
+template <int NW, int RF, int MF, int MODE, int KS, bool FP4>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nrows, int rb, uint16_t* lds) {
+  constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+  constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;  // token planes (h hi and lo for down)
+  constexpr int BM = MF * 16;
+  constexpr int SUB = KS / 32;       // MFMA sub-steps per step
+  constexpr int LROW = KS + 8;       // LDS row stride (bf16), 16-byte pad against bank conflicts
+  constexpr int NTH = NW * 64;
+  constexpr int CHUNKS = BM * KS / 8;  // 16-byte pieces of one token plane per step
+  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
+  constexpr int ROWS = NW * RF * 16;
+  constexpr int WREGS = FP4 ? 1 : SUB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N;
+  const int nsteps = K / KS;
+  const bool shared = e == a.E;
+  const int pos0 = a.offsets[e] + m0;
+
+  // token tile: per-thread 16-byte pieces (row, col) and their sources (null -> zeros)
+  const uint16_t* tsrc[NTP][CPT];
+  int tdst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * NTH;
+#pragma unroll
+    for (int p = 0; p < NTP; ++p) tsrc[p][i] = nullptr;
+    tdst[i] = -1;
+    if (c < CHUNKS) {
+      const int row = c / (KS / 8), col = (c % (KS / 8)) * 8;
+      tdst[i] = row * LROW + col;
+      if (row < nrows) {
+        if (MODE == MODE_GATEUP) {
+          const int tok = a.sorted_token[pos0 + row];
+          if ((unsigned)tok < (unsigned)a.T) tsrc[0][i] = a.act + (size_t)tok * K + col;
+        } else {
+          tsrc[0][i] = a.act + (size_t)(pos0 + row) * K + col;
+          tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + row) * K + col;
+        }
+      }
+    }
+  }
+
+  // weight rows of this lane
+  const int nbase = rb * ROWS + wave * RF * 16;
+  const uint16_t* wp[NMAT][RF];
+  const uint8_t* wq[NMAT][RF];
+  const uint8_t* wsc[NMAT][RF];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      const size_t row = (size_t)(nbase + f * 16 + r16);
+      if constexpr (FP4) {
+        const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / 2);
+        const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
+        wq[m][f] = base + row * (K / 2) + q * (KS / 8);
+        wsc[m][f] = sbase + row * (K / 32) + q * (KS / 128);
+        wp[m][f] = nullptr;
+      } else {
+        const uint16_t* base = shared ? (const uint16_t*)(m == 0 ? a.sw0 : a.sw1)
+                                      : (const uint16_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * K;
+        wp[m][f] = base + row * K + q * (KS / 4);
+        wq[m][f] = nullptr;
+        wsc[m][f] = nullptr;
+      }
+    }
+
+  floatx4 acc[NMAT][RF][MF];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 treg[NTP][CPT];
+  auto load_t = [&](int step) {
+#pragma unroll
+    for (int p = 0; p < NTP; ++p)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        treg[p][i] = tsrc[p][i] ? *(const u32x4*)(tsrc[p][i] + step * KS) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_t = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < NTP; ++p)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (tdst[i] >= 0) *(u32x4*)(lds + (buf * NTP + p) * BM * LROW + tdst[i]) = treg[p][i];
+  };
+  auto load_w = [&](WStage<NMAT, RF, WREGS>& st, int step) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        if constexpr (FP4) {
+          st.w[m][f][0] = *(const u32x4*)(wq[m][f] + (size_t)step * (KS / 2));
+          st.sc[m][f] = wsc[m][f][(size_t)step * (KS / 32)];
+        } else {
+#pragma unroll
+          for (int s = 0; s < WREGS; ++s) st.w[m][f][s] = *(const u32x4*)(wp[m][f] + (size_t)step * KS + s * 8);
+        }
+      }
+  };
+  auto compute = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
+    const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW + q * (KS / 4);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      u32x4 tf[NTP][MF];
+#pragma unroll
+      for (int p = 0; p < NTP; ++p)
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) tf[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + s * 8);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          u32x4 wf;
+          if constexpr (FP4) {
+            wf = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+          } else {
+            wf = st.w[m][f][s];
+          }
+#pragma unroll
+          for (int p = NTP - 1; p >= 0; --p)
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = mfma16(wf, tf[p][mf], acc[m][f][mf]);
+        }
+    }
+  };
+
+  WStage<NMAT, RF, WREGS> sa, sb;
+  load_t(0);
+  load_w(sa, 0);
+  store_t(0);
+  if (nsteps > 1) {
+    load_t(1);
+    load_w(sb, 1);
+  }
+  block_sync_lds();
+  for (int s = 0; s < nsteps; s += 2) {
+    compute(sa, 0);
+    if (s + 1 < nsteps) store_t(1);
+    if (s + 2 < nsteps) {
+      load_t(s + 2);
+      load_w(sa, s + 2);
+    }
+    block_sync_lds();
+    if (s + 1 >= nsteps) break;
+    compute(sb, 1);
+    if (s + 2 < nsteps) store_t(0);
+    if (s + 3 < nsteps) {
+      load_t(s + 3);
+      load_w(sb, s + 3);
+    }
+    block_sync_lds();
+  }
+
+  // epilogue: lane holds token r16 of each fragment and rows 4q .. 4q+3 of each 16-row block
+  const float limit = shared ? a.shared_limit : a.limit;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int j = mf * 16 + r16;
+    if (j >= nrows) continue;
+    const size_t obase = (size_t)(pos0 + j) * N + nbase + 4 * q;
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      if (MODE == MODE_GATEUP) {
+        float hv[4], lv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[0][f][mf][r], u = acc[NMAT - 1][f][mf][r];
+          float h = g / (1.0f + __expf(-g)) * u;
+          if (limit > 0.f) h = fminf(fmaxf(h, -limit), limit);
+          hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
+          lv[r] = h - hv[r];  // exact in fp32
+        }
+        *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+      } else {
+        *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][mf];
+      }
+    }
+  }
+}
+
+template <int NW, int RF, int MF, int MODE, int FMT>
+__global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
+  constexpr int KS = FMT == FMT_MXFP4 ? 128 : 64;
+  constexpr int BM = MF * 16;
+  constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
+  __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 8)];
+
+  // device work list: work id -> (tile, row block); tiles of one XCD are consecutive
+  const int total = a.tile_prefix[a.E + a.S] * a.nrb;
+  const int per_xcd = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return;
+  const int w = (blockIdx.x & 7) * per_xcd + slot;
+  if (w >= total) return;
+  const int tile = w / a.nrb, rb = w - tile * a.nrb;
+  int lo = 0, hi = a.E + a.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_prefix[mid] <= tile) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int m0 = (tile - a.tile_prefix[e]) * BM;
+  const int cnt = a.offsets[e + 1] - a.offsets[e];
+  const int nrows = min(BM, cnt - m0);
+  if constexpr (FMT == FMT_MXFP4) {
+    if (e < a.E) {
+      ffn_tile<NW, RF, MF, MODE, KS, true>(a, e, m0, nrows, rb, lds);
+      return;
+    }
+  }
+  ffn_tile<NW, RF, MF, MODE, KS, false>(a, e, m0, nrows, rb, lds);
+}
+
+// single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan
+__global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int n, int bm,
+                                                         int32_t* __restrict__ tile_prefix) {
+  const int lane = threadIdx.x;
+  const int per = (n + WAVE - 1) / WAVE;
+  const int b = lane * per, e = min(n, b + per);
+  int sum = 0;
+  for (int i = b; i < e; ++i) sum += (offsets[i + 1] - offsets[i] + bm - 1) / bm;
+  int incl = sum;
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) {
+    int o = __shfl_up(incl, m, WAVE);
+    if (lane >= m) incl += o;
+  }
+  int run = incl - sum;
+  if (lane == 0) tile_prefix[0] = 0;
+  for (int i = b; i < e; ++i) {
+    run += (offsets[i + 1] - offsets[i] + bm - 1) / bm;
+    tile_prefix[i + 1] = run;
+  }
+}
+
+constexpr int FFN_NW = 4, FFN_RF = 2, FFN_ROWS = FFN_NW * FFN_RF * 16;
+
+template <int MF, int MODE, int FMT>
+hipError_t launch_one(const FfnArgs& a, int64_t max_tiles, hipStream_t s, Tracer* tr) {
+  int64_t work = max_tiles * a.nrb;
+  int64_t grid = (work + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((ffn_kernel<FFN_NW, FFN_RF, MF, MODE, FMT>), dim3((unsigned)grid), dim3(FFN_NW * 64), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (tr) tr->mark(MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
+  return err;
+}
+
+template <int MF>
+hipError_t launch_mf(const FfnArgs& gu, const FfnArgs& dn, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr) {
+  hipError_t err;
+  if (fmt == FMT_MXFP4) {
+    err = launch_one<MF, MODE_GATEUP, FMT_MXFP4>(gu, max_tiles, s, tr);
+    if (err != hipSuccess) return err;
+    return launch_one<MF, MODE_DOWN, FMT_MXFP4>(dn, max_tiles, s, tr);
+  }
+  err = launch_one<MF, MODE_GATEUP, FMT_BF16>(gu, max_tiles, s, tr);
+  if (err != hipSuccess) return err;
+  return launch_one<MF, MODE_DOWN, FMT_BF16>(dn, max_tiles, s, tr);
+}
+
+}  // namespace
+
+FfnPlan ffn_plan(int64_t T, int K, int E, int S) {
+  FfnPlan p;
+  const double avg = (double)T * K / E;  // routed tokens per expert on average
+  p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : 8;
+  p.bm = 16 * p.mf;
+  const int64_t pairs = T * K + T * S;
+  p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
+  return p;
+}
+
+hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
+                             int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
+                             float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
+                             hipStream_t s, Tracer* tr) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
+  hipError_t err = hipGetLastError();
+  if (tr) tr->mark("expert_tiles", s);
+  if (err != hipSuccess) return err;
+
+  FfnArgs gu{};
+  gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
+  gu.w0 = w.gate; gu.w1 = w.up; gu.s0 = w.gate_scale; gu.s1 = w.up_scale;
+  gu.sw0 = w.sh_gate; gu.sw1 = w.sh_up; gu.out = h_hi; gu.out_lo = h_lo;
+  gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I; gu.nrb = I / FFN_ROWS;
+  gu.limit = limit; gu.shared_limit = shared_limit;
+
+  FfnArgs dn = gu;
+  dn.act = h_hi; dn.act_lo = h_lo; dn.sorted_token = nullptr; dn.out_lo = nullptr;
+  dn.w0 = w.down; dn.w1 = nullptr; dn.s0 = w.down_scale; dn.s1 = nullptr;
+  dn.sw0 = w.sh_down; dn.sw1 = nullptr; dn.out = y;
+  dn.K = I; dn.N = H; dn.nrb = H / FFN_ROWS;
+
+  switch (p.mf) {
+    case 1: return launch_mf<1>(gu, dn, w.fmt, p.max_tiles, s, tr);
+    case 2: return launch_mf<2>(gu, dn, w.fmt, p.max_tiles, s, tr);
+    case 4: return launch_mf<4>(gu, dn, w.fmt, p.max_tiles, s, tr);
+    default: return launch_mf<8>(gu, dn, w.fmt, p.max_tiles, s, tr);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,353 @@
+// C-ABI host layer of libmoe: argument validation (pure host code, before any HIP call),
+// workspace layout and launch sequencing on the caller's stream.  The declarations and the
+// contract of every entry point are in include/moe.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define MOE_CHECK_PTR(p, name)                                                            \
+  do {                                                                                    \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s must not be NULL", name);              \
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGNMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define MOE_CHECK_OPT_PTR(p, name)                                                               \
+  do {                                                                                           \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_ALIGNMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+moe_status_t validate_config(const moe_config_t* c, int64_t T) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg must not be NULL");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)T);
+  if (c->hidden_size <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be > 0");
+  if (c->hidden_size % 128) return fail(MOE_ERR_UNSUPPORTED, "hidden_size %d is not a multiple of 128", c->hidden_size);
+  const int E = c->num_experts;
+  if (E <= 0) return fail(MOE_ERR_INVALID_ARG, "num_experts must be > 0");
+  if (E % 64 || E > 1024 || ((E / 64) & (E / 64 - 1)))
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts %d must be 64 * 2^k and at most 1024", E);
+  const int G = c->n_group;
+  if (G <= 0 || E % G) return fail(MOE_ERR_INVALID_ARG, "n_group %d must divide num_experts %d", G, E);
+  if (64 % G) return fail(MOE_ERR_UNSUPPORTED, "n_group %d must divide 64", G);
+  if (c->topk_group < 1 || c->topk_group > G)
+    return fail(MOE_ERR_INVALID_ARG, "topk_group %d must be in [1, n_group=%d]", c->topk_group, G);
+  const int K = c->num_experts_per_tok;
+  if (K < 1 || K > c->topk_group * (E / G))
+    return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d must be in [1, topk_group*E/n_group=%d]", K,
+                c->topk_group * (E / G));
+  if (K > 16) return fail(MOE_ERR_UNSUPPORTED, "num_experts_per_tok %d is above 16", K);
+  if (c->moe_intermediate_size <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_intermediate_size must be > 0");
+  if (c->moe_intermediate_size % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_intermediate_size %d is not a multiple of 128", c->moe_intermediate_size);
+  if (c->num_shared_experts < 0 || c->num_shared_experts > 1)
+    return fail(MOE_ERR_INVALID_ARG, "num_shared_experts %d must be 0 or 1", c->num_shared_experts);
+  if (c->num_shared_experts && c->shared_intermediate_size != c->moe_intermediate_size)
+    return fail(MOE_ERR_UNSUPPORTED, "shared_intermediate_size %d must equal moe_intermediate_size %d",
+                c->shared_intermediate_size, c->moe_intermediate_size);
+  if (c->expert_weight_format != MOE_WEIGHTS_BF16 && c->expert_weight_format != MOE_WEIGHTS_MXFP4)
+    return fail(MOE_ERR_INVALID_ARG, "expert_weight_format %d is unknown", c->expert_weight_format);
+  if (!std::isfinite(c->routed_scaling_factor)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor is not finite");
+  if (std::isnan(c->swiglu_limit) || std::isnan(c->shared_swiglu_limit))
+    return fail(MOE_ERR_INVALID_ARG, "swiglu limits must not be NaN");
+  if (T > (int64_t)((1u << 31) - 1) / (K + 1))
+    return fail(MOE_ERR_UNSUPPORTED, "T = %lld is too large for 32-bit positions", (long long)T);
+  return MOE_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t partial, bitmap, counts, offsets, tile_prefix, topk_idx, topk_w, sorted_token, inv_perm, h_hi, h_lo, y,
+      total;
+};
+
+Layout layout(const moe_config_t* c, int64_t T) {
+  const int64_t E = c->num_experts, K = c->num_experts_per_tok, H = c->hidden_size, I = c->moe_intermediate_size;
+  const int64_t S = c->num_shared_experts;
+  const int64_t P = T * K + T * S;
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.partial = take(moe::router_partial_bytes(T, (int)H, (int)E));
+  L.bitmap = take(moe::dispatch_bitmap_words(T, (int)E) * 4);
+  L.counts = take((E + 1) * 4);
+  L.offsets = take((E + 2) * 4);
+  L.tile_prefix = take((E + 2) * 4);
+  L.topk_idx = take(T * K * 4);
+  L.topk_w = take(T * K * 4);
+  L.sorted_token = take(P * 4);
+  L.inv_perm = take(T * K * 4);
+  L.h_hi = take(P * I * 2);
+  L.h_lo = take(P * I * 2);
+  L.y = take(P * H * 4);
+  L.total = off;
+  return L;
+}
+
+moe_status_t check_ws(const moe_config_t* c, int64_t T, const void* ws, size_t ws_bytes, Layout* out) {
+  Layout L = layout(c, T);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace must not be NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", ws_bytes, L.total, (long long)T);
+  *out = L;
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_config_t* c, const moe_expert_weights_t* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights must not be NULL");
+  MOE_CHECK_PTR(w->gate, "weights->gate");
+  MOE_CHECK_PTR(w->up, "weights->up");
+  MOE_CHECK_PTR(w->down, "weights->down");
+  if (c->expert_weight_format == MOE_WEIGHTS_MXFP4) {
+    if (!w->gate_scale || !w->up_scale || !w->down_scale)
+      return fail(MOE_ERR_INVALID_ARG, "MXFP4 weights need gate_scale, up_scale and down_scale");
+  }
+  if (c->num_shared_experts) {
+    MOE_CHECK_PTR(w->shared_gate, "weights->shared_gate");
+    MOE_CHECK_PTR(w->shared_up, "weights->shared_up");
+    MOE_CHECK_PTR(w->shared_down, "weights->shared_down");
+  }
+  return MOE_OK;
+}
+
+moe::FfnWeights ffn_weights(const moe_config_t* c, const moe_expert_weights_t* w) {
+  moe::FfnWeights f{};
+  f.gate = w->gate; f.up = w->up; f.down = w->down;
+  f.gate_scale = w->gate_scale; f.up_scale = w->up_scale; f.down_scale = w->down_scale;
+  f.sh_gate = w->shared_gate; f.sh_up = w->shared_up; f.sh_down = w->shared_down;
+  f.fmt = c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16;
+  return f;
+}
+
+char* at(void* ws, size_t off) { return (char*)ws + off; }
+
+moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const float* rw, const float* bias,
+                      int32_t* idx, float* wts, const Layout& L, void* ws, hipStream_t s,
+                      moe::Tracer* tr = nullptr) {
+  moe::RouterPlan p = moe::router_plan(T, c->hidden_size, c->num_experts);
+  float* partial = (float*)at(ws, L.partial);
+  hipError_t e = moe::launch_router_logits(p, (const uint16_t*)x, rw, (int)T, c->hidden_size, c->num_experts,
+                                           partial, s, tr);
+  if (e != hipSuccess) return hip_fail(e, "router logits launch");
+  e = moe::launch_router_topk(partial, p.nsplit, (int)T, c->num_experts, bias, c->n_group, c->topk_group,
+                              c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, s, tr);
+  if (e != hipSuccess) return hip_fail(e, "router top-k launch");
+  return MOE_OK;
+}
+
+moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_token, int32_t* inv_perm, const Layout& L, void* ws, hipStream_t s,
+                         moe::Tracer* tr = nullptr) {
+  hipError_t e = moe::launch_dispatch(idx, (int)T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
+                                      (uint32_t*)at(ws, L.bitmap), counts, offsets, sorted_token, inv_perm, s, tr);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  return MOE_OK;
+}
+
+moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32_t* offsets,
+                    const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
+                    hipStream_t s, moe::Tracer* tr = nullptr) {
+  moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts);
+  const float lim = c->swiglu_limit > 0 ? c->swiglu_limit : 0.f;
+  const float slim = c->shared_swiglu_limit > 0 ? c->shared_swiglu_limit : 0.f;
+  hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),
+                                        ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
+                                        c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
+                                        (uint16_t*)at(ws, L.h_lo), (float*)y, s, tr);
+  if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
+  return MOE_OK;
+}
+
+moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* y, const int32_t* inv, const float* wts,
+                        void* out, hipStream_t s, moe::Tracer* tr = nullptr) {
+  hipError_t e = moe::launch_combine((const float*)y, inv, wts, (int)T, c->num_experts_per_tok, c->hidden_size,
+                                     c->num_shared_experts, (uint16_t*)out, s, tr);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_ALIGNMENT: return "MOE_ERR_ALIGNMENT";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status_t";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes must not be NULL");
+  *bytes = layout(cfg, T).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                       const float* expert_bias, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(router_w, "router_w");
+  MOE_CHECK_OPT_PTR(expert_bias, "expert_bias");
+  MOE_CHECK_PTR(topk_idx, "topk_idx");
+  MOE_CHECK_PTR(topk_w, "topk_w");
+  Layout L;
+  if ((st = check_ws(cfg, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return do_route(cfg, T, x, router_w, expert_bias, topk_idx, topk_w, L, ws, (hipStream_t)stream);
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(topk_idx, "topk_idx");
+  MOE_CHECK_PTR(expert_counts, "expert_counts");
+  MOE_CHECK_PTR(expert_offsets, "expert_offsets");
+  MOE_CHECK_PTR(sorted_token, "sorted_token");
+  MOE_CHECK_PTR(inv_perm, "inv_perm");
+  Layout L;
+  if ((st = check_ws(cfg, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return do_dispatch(cfg, T, topk_idx, expert_counts, expert_offsets, sorted_token, inv_perm, L, ws,
+                     (hipStream_t)stream);
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x, const int32_t* expert_offsets,
+                            const int32_t* sorted_token, const moe_expert_weights_t* weights, void* y_sorted, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(expert_offsets, "expert_offsets");
+  MOE_CHECK_PTR(sorted_token, "sorted_token");
+  MOE_CHECK_PTR(y_sorted, "y_sorted");
+  if ((st = check_weights(cfg, weights)) != MOE_OK) return st;
+  Layout L;
+  if ((st = check_ws(cfg, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return do_ffn(cfg, T, x, expert_offsets, sorted_token, weights, y_sorted, L, ws, (hipStream_t)stream);
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_sorted, const int32_t* inv_perm,
+                         const float* topk_w, void* out, void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(y_sorted, "y_sorted");
+  MOE_CHECK_PTR(inv_perm, "inv_perm");
+  MOE_CHECK_PTR(topk_w, "topk_w");
+  MOE_CHECK_PTR(out, "out");
+  return do_combine(cfg, T, y_sorted, inv_perm, topk_w, out, (hipStream_t)stream);
+}
+
+namespace {
+
+moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                          const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                          int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                          size_t ws_bytes, void* stream, moe::Tracer* tr) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(router_w, "router_w");
+  MOE_CHECK_OPT_PTR(expert_bias, "expert_bias");
+  MOE_CHECK_PTR(out, "out");
+  MOE_CHECK_OPT_PTR(topk_idx_out, "topk_idx_out");
+  MOE_CHECK_OPT_PTR(topk_w_out, "topk_w_out");
+  MOE_CHECK_OPT_PTR(expert_counts_out, "expert_counts_out");
+  if ((st = check_weights(cfg, weights)) != MOE_OK) return st;
+  Layout L;
+  if ((st = check_ws(cfg, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)at(ws, L.topk_idx);
+  float* wts = topk_w_out ? topk_w_out : (float*)at(ws, L.topk_w);
+  int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)at(ws, L.counts);
+  int32_t* offsets = (int32_t*)at(ws, L.offsets);
+  int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
+  int32_t* inv = (int32_t*)at(ws, L.inv_perm);
+  void* y = at(ws, L.y);
+  if (tr && tr->events && tr->cap > 0) hipEventRecord(tr->events[0], s);
+  if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr)) != MOE_OK) return st;
+  if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr)) != MOE_OK) return st;
+  if ((st = do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr)) != MOE_OK) return st;
+  return do_combine(cfg, T, y, inv, wts, out, s, tr);
+}
+
+}  // namespace
+
+moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                         const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                         int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, T, x, router_w, expert_bias, weights, out, topk_idx_out, topk_w_out, expert_counts_out,
+                      ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_forward_traced(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                                void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t max_events,
+                                const char** kernel_names, int32_t* n_kernels) {
+  if (!events || max_events < 1 || !kernel_names || !n_kernels)
+    return fail(MOE_ERR_INVALID_ARG, "events, kernel_names and n_kernels are required, max_events >= 1");
+  moe::Tracer tr;
+  tr.events = (hipEvent_t*)events;
+  tr.names = kernel_names;
+  tr.cap = max_events;
+  moe_status_t st = forward_impl(cfg, T, x, router_w, expert_bias, weights, out, nullptr, nullptr, nullptr, ws,
+                                 ws_bytes, stream, &tr);
+  *n_kernels = tr.n;
+  if (st == MOE_OK && tr.n + 1 > max_events)
+    return fail(MOE_ERR_INVALID_ARG, "%d kernels launched but only %d events given", tr.n, max_events);
+  return st;
+}
+
+}  // extern "C"

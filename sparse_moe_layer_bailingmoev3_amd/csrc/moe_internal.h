@@ -1,0 +1,70 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { FMT_BF16 = 0, FMT_MXFP4 = 1 };
+
+// Optional per-kernel event trace: events[0] is recorded by the caller before the first
+// launch, events[i+1] right after the i-th kernel; names[i] names that kernel.
+struct Tracer {
+  hipEvent_t* events = nullptr;
+  const char** names = nullptr;
+  int cap = 0;  // number of events available
+  int n = 0;    // kernels launched so far
+  void mark(const char* name, hipStream_t s) {
+    if (events && n + 1 < cap) {
+      hipEventRecord(events[n + 1], s);
+      names[n] = name;
+    }
+    ++n;
+  }
+};
+
+// ---- router ------------------------------------------------------------------
+struct RouterPlan {
+  int mf;       // 16-token fragments per workgroup (1, 2, 4 or 8)
+  int rf;       // 16-expert blocks per wave (1 or 2)
+  int nsplit;   // split of the hidden dimension (partial logits summed in order)
+  int m_tiles, n_tiles;
+};
+RouterPlan router_plan(int64_t T, int H, int E);
+size_t router_partial_bytes(int64_t T, int H, int E);
+hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const float* w, int T, int H,
+                                int E, float* partial, hipStream_t s, Tracer* tr = nullptr);
+hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G,
+                              int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
+                              hipStream_t s, Tracer* tr = nullptr);
+
+// ---- dispatch ----------------------------------------------------------------
+size_t dispatch_bitmap_words(int64_t T, int E);
+hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, uint32_t* bitmap,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                           hipStream_t s, Tracer* tr = nullptr);
+
+// ---- expert FFN --------------------------------------------------------------
+struct FfnWeights {
+  const void* gate; const void* up; const void* down;
+  const uint8_t* gate_scale; const uint8_t* up_scale; const uint8_t* down_scale;
+  const void* sh_gate; const void* sh_up; const void* sh_down;
+  int fmt;
+};
+struct FfnPlan {
+  int mf;      // 16-token fragments per tile
+  int bm;      // tokens per tile = 16 * mf
+  int64_t max_tiles;
+};
+FfnPlan ffn_plan(int64_t T, int K, int E, int S);
+hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
+                             const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
+                             int T, int H, int I, int E, int S, float limit, float shared_limit,
+                             uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr = nullptr);
+
+// ---- combine -----------------------------------------------------------------
+hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,
+                          int K, int H, int S, uint16_t* out, hipStream_t s, Tracer* tr = nullptr);
+
+}  // namespace moe

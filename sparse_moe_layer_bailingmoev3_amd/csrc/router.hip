@@ -1,0 +1,286 @@
+// Router of the BailingMoeV3 sparse MoE block.
+//
+// Ling-3.0-flash-VL routing walk-through page (lqnn.cn), section 三.1: one raw score per
+// routed expert from the hidden state, then an element-wise sigmoid; section 三.3: a
+// per-expert bias is added for selection; section 三.2: keep the topk_group groups with the
+// largest in-group maximum and pick the top-k experts inside them; section 四: the router
+// runs in fp32, the chosen scores are renormalised and scaled by routed_scaling_factor.
+//
+// Two kernels:
+//   router_logits_kernel  fp32-accurate logits on bf16 MFMA.  x is bf16, so splitting each
+//                         fp32 router weight exactly into three bf16 pieces (hi + mid + lo,
+//                         8 significand bits each) makes every product x * piece exact in
+//                         fp32; three 16x16x32 bf16 MFMAs with fp32 accumulation then give
+//                         fp32-GEMM logits at a fraction of the cost of fp32 MFMA (the
+//                         split-precision idea of Markidis et al. 2018 / Ootomo & Yokota
+//                         2022).  The hidden dimension may be split across workgroups for
+//                         small token counts; partial sums are added later in a fixed order.
+//   router_topk_kernel    one wave per token: sigmoid, bias, group max, group ranking and the
+//                         top-k selection entirely in registers with wave shuffles.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  // exact split by truncation: w = hi + mid + lo, each a bf16
+  uint32_t u0 = __float_as_uint(w0), u1 = __float_as_uint(w1);
+  uint32_t h0 = u0 & 0xFFFF0000u, h1 = u1 & 0xFFFF0000u;
+  float r0 = w0 - __uint_as_float(h0), r1 = w1 - __uint_as_float(h1);
+  uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u, m1 = __float_as_uint(r1) & 0xFFFF0000u;
+  float s0 = r0 - __uint_as_float(m0), s1 = r1 - __uint_as_float(m1);
+  uint32_t l0 = __float_as_uint(s0) & 0xFFFF0000u, l1 = __float_as_uint(s1) & 0xFFFF0000u;
+  hi = (h0 >> 16) | h1;
+  mid = (m0 >> 16) | m1;
+  lo = (l0 >> 16) | l1;
+}
+
+// partial[split][t][e] = sum over the split's slice of h of x[t][h] * W[e][h].
+// Workgroup: 4 waves; wave w owns RF 16-row blocks of experts (the MFMA a operands),
+// tokens m0 .. m0 + 16*MF - 1 are the b operands.  Lane (r, q) of a 16x32 operand holds
+// row r, k = kb + 8q .. kb + 8q + 7.
+template <int MF, int RF>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ w, int T, int H,
+                                                            int E, int kchunk, float* __restrict__ partial) {
+  constexpr int WG_EXPERTS = 4 * RF * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int n_tiles = E / WG_EXPERTS;
+  const int nt = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
+  const int m0 = blockIdx.y * 16 * MF;
+  const int e_base = nt * WG_EXPERTS + wave * RF * 16;
+  const int k0 = split * kchunk;
+
+  const float* wr[RF];
+#pragma unroll
+  for (int f = 0; f < RF; ++f) wr[f] = w + (size_t)(e_base + f * 16 + r16) * H + k0 + q * 8;
+  const uint16_t* xr[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    int t = min(m0 + mf * 16 + r16, T - 1);
+    xr[mf] = x + (size_t)t * H + k0 + q * 8;
+  }
+  floatx4 acc[RF][MF];
+#pragma unroll
+  for (int f = 0; f < RF; ++f)
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) acc[f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kk = 0; kk < kchunk; kk += 32) {
+    float4 a[RF][2];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      a[f][0] = *(const float4*)(wr[f] + kk);
+      a[f][1] = *(const float4*)(wr[f] + kk + 4);
+    }
+    u32x4 xv[MF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) xv[mf] = *(const u32x4*)(xr[mf] + kk);
+    u32x4 hi[RF], mid[RF], lo[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      const float v[8] = {a[f][0].x, a[f][0].y, a[f][0].z, a[f][0].w, a[f][1].x, a[f][1].y, a[f][1].z, a[f][1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h, m, l;
+        split3(v[2 * i], v[2 * i + 1], h, m, l);
+        hi[f][i] = h;
+        mid[f][i] = m;
+        lo[f][i] = l;
+      }
+    }
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        acc[f][mf] = mfma16(lo[f], xv[mf], acc[f][mf]);
+        acc[f][mf] = mfma16(mid[f], xv[mf], acc[f][mf]);
+        acc[f][mf] = mfma16(hi[f], xv[mf], acc[f][mf]);
+      }
+  }
+  // result: lane holds token r16 of each fragment, experts 4q .. 4q+3 of each 16-row block
+  float* out = partial + (size_t)split * T * E;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    int t = m0 + mf * 16 + r16;
+    if (t < T) {
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        float4 v = {acc[f][mf][0], acc[f][mf][1], acc[f][mf][2], acc[f][mf][3]};
+        *(float4*)(out + (size_t)t * E + e_base + f * 16 + 4 * q) = v;
+      }
+    }
+  }
+}
+
+// One wave per token.  Lane l holds experts l*EPL .. l*EPL + EPL - 1, so a group of E/G
+// experts is 64/G consecutive lanes.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
+                                                          int T, int E, const float* __restrict__ bias, int G,
+                                                          int TG, int K, int norm, float scale,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int e0 = lane * EPL;
+
+  // logits: split partial sums added in split order
+  float l[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) l[i] = 0.f;
+  for (int p = 0; p < nsplit; ++p) {
+    const float* src = partial + ((size_t)p * T + t) * E + e0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) l[i] += src[i];
+  }
+
+  // sigmoid score s and biased choice score c
+  float s[EPL], c[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    s[i] = 1.0f / (1.0f + expf(-l[i]));
+    float b = bias ? bias[e0 + i] : 0.0f;
+    c[i] = (s[i] + b) + 0.0f;  // + 0 turns a -0 into +0 so equal scores compare as ties
+  }
+
+  // group score: maximum biased score inside the group
+  const int lpg = WAVE / G;
+  float gm = c[0];
+#pragma unroll
+  for (int i = 1; i < EPL; ++i) gm = fmaxf(gm, c[i]);
+  for (int m = 1; m < lpg; m <<= 1) gm = fmaxf(gm, __shfl_xor(gm, m, WAVE));
+
+  // rank of this lane's group among all groups (ties: lower group index first)
+  const int g = lane / lpg;
+  int rank = 0;
+  for (int h = 0; h < G; ++h) {
+    float o = __shfl(gm, h * lpg, WAVE);
+    rank += (o > gm) || (o == gm && h < g);
+  }
+  const bool kept = rank < TG;
+
+  // selection keys: ordered score in the high word, reversed index in the low word, so
+  // the maximum key is the best score and, among equal scores, the lowest index.
+  // Experts of dropped groups get key 0 and can never be chosen.
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    key[i] = kept ? (((uint64_t)f32_ordered(c[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(e0 + i))) : 0ull;
+
+  int my_idx = 0;
+  float my_s = 0.f;
+  for (int r = 0; r < K; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int idx = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const int owner = idx / EPL, slot = idx - owner * EPL;
+    float sv = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (i == slot) {
+        sv = s[i];
+        if (lane == owner) key[i] = 0ull;
+      }
+    }
+    sv = __shfl(sv, owner, WAVE);
+    if (lane == r) {
+      my_idx = idx;
+      my_s = sv;
+    }
+  }
+
+  // renormalise (unbiased scores) and scale; write in ascending expert order
+  const float sum = wave_sum_f32(lane < K ? my_s : 0.f);
+  int pos = 0;
+  for (int j = 0; j < K; ++j) pos += __shfl(my_idx, j, WAVE) < my_idx;
+  if (lane < K) {
+    const float wv = norm ? (my_s / sum) * scale : my_s * scale;
+    topk_idx[(size_t)t * K + pos] = my_idx;
+    topk_w[(size_t)t * K + pos] = wv;
+  }
+}
+
+int pick_router_mf(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8; }
+
+}  // namespace
+
+RouterPlan router_plan(int64_t T, int H, int E) {
+  RouterPlan p;
+  p.mf = pick_router_mf(T);
+  p.m_tiles = (int)((T + 16 * p.mf - 1) / (16 * p.mf));
+  p.rf = (E % 128 == 0) ? 2 : 1;
+  p.n_tiles = E / (64 * p.rf);
+  // split the hidden dimension until ~256 workgroups exist (the chip has 256 CUs); each
+  // split is a multiple of 32 that divides H
+  const int kb = H / 32;
+  int best = 1;
+  for (int ns = 1; ns <= kb; ++ns) {
+    if (kb % ns) continue;
+    if ((int64_t)p.m_tiles * p.n_tiles * ns > 320) break;
+    best = ns;
+  }
+  p.nsplit = best;
+  return p;
+}
+
+size_t router_partial_bytes(int64_t T, int H, int E) {
+  RouterPlan p = router_plan(T, H, E);
+  return (size_t)p.nsplit * (size_t)T * (size_t)E * sizeof(float);
+}
+
+hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const float* w, int T, int H, int E,
+                                float* partial, hipStream_t s, Tracer* tr) {
+  dim3 grid(p.n_tiles * p.nsplit, p.m_tiles), block(256);
+  const int kchunk = H / p.nsplit;
+#define MOE_RL(M, R) hipLaunchKernelGGL((router_logits_kernel<M, R>), grid, block, 0, s, x, w, T, H, E, kchunk, partial)
+  if (p.rf == 2) {
+    switch (p.mf) {
+      case 1: MOE_RL(1, 2); break;
+      case 2: MOE_RL(2, 2); break;
+      case 4: MOE_RL(4, 2); break;
+      default: MOE_RL(8, 2); break;
+    }
+  } else {
+    switch (p.mf) {
+      case 1: MOE_RL(1, 1); break;
+      case 2: MOE_RL(2, 1); break;
+      case 4: MOE_RL(4, 1); break;
+      default: MOE_RL(8, 1); break;
+    }
+  }
+#undef MOE_RL
+  hipError_t err = hipGetLastError();
+  if (tr) tr->mark("router_logits", s);
+  return err;
+}
+
+hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G, int TG,
+                              int K, int norm, float scale, int32_t* topk_idx, float* topk_w, hipStream_t s,
+                              Tracer* tr) {
+  dim3 grid((T + 3) / 4), block(256);
+  const int epl = E / WAVE;
+#define MOE_TOPK(N)                                                                                          \
+  hipLaunchKernelGGL(router_topk_kernel<N>, grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, norm, \
+                     scale, topk_idx, topk_w)
+  switch (epl) {
+    case 1: MOE_TOPK(1); break;
+    case 2: MOE_TOPK(2); break;
+    case 4: MOE_TOPK(4); break;
+    case 8: MOE_TOPK(8); break;
+    case 16: MOE_TOPK(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_TOPK
+  hipError_t err = hipGetLastError();
+  if (tr) tr->mark("router_topk", s);
+  return err;
+}
+
+}  // namespace moe

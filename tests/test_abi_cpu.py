@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point, sizes its
+workspace, and rejects bad arguments on the host before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_bailingmoev3_amd as moe
+from synthetic import CONFIGS
+
+from moe_case import cfg_for
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.lib_path()), reason="libmoe.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size",
+              "moe_status_string", "moe_last_error"):
+        assert n in names
+    assert set(names) == set(moe.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert moe.moe_status_string(0) == "MOE_OK"
+    assert moe.moe_status_string(-4) == "MOE_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_size_grows_with_T(name):
+    cfg = cfg_for(CONFIGS[name])
+    a = moe.moe_workspace_size(cfg, 64)
+    b = moe.moe_workspace_size(cfg, 8192)
+    assert 0 < a < b
+    s = CONFIGS[name]
+    # the workspace holds at least the sorted activations and expert outputs
+    P = 8192 * (s.K + 1)
+    assert b >= P * (s.I + s.H) * 2
+
+
+def _bad(cfg_kw, T=64, code=None):
+    cfg = cfg_for(CONFIGS["decode"])
+    for k, v in cfg_kw.items():
+        setattr(cfg, k, v)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_workspace_size(cfg, T)
+    if code is not None:
+        assert ei.value.status == code, str(ei.value)
+    return str(ei.value)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_experts=500), -2),            # not 64 * 2^k
+    (dict(n_group=7), -1),                   # does not divide E
+    (dict(n_group=128, num_experts=1024), -2),  # does not divide 64
+    (dict(topk_group=9), -1),
+    (dict(topk_group=0), -1),
+    (dict(num_experts_per_tok=0), -1),
+    (dict(num_experts_per_tok=300, topk_group=4), -1),  # more than the 256 candidates
+    (dict(num_experts_per_tok=17), -2),
+    (dict(hidden_size=2500), -2),
+    (dict(hidden_size=-128), -1),
+    (dict(moe_intermediate_size=700), -2),
+    (dict(num_shared_experts=2), -1),
+    (dict(shared_intermediate_size=1024), -2),
+    (dict(expert_weight_format=7), -1),
+    (dict(routed_scaling_factor=float("inf")), -1),
+    (dict(swiglu_limit=float("nan")), -1),
+])
+def test_config_validation(kw, code):
+    _bad(kw, code=code)
+
+
+def test_negative_T():
+    _bad({}, T=-1, code=-1)
+
+
+def test_entry_points_reject_bad_pointers_before_any_launch():
+    cfg = cfg_for(CONFIGS["decode"])
+    lib = moe.load_library()
+    T = 64
+    need = moe.moe_workspace_size(cfg, T)
+    fake = 1 << 40          # an aligned address that is never dereferenced: validation fails first
+    w = moe.MoEExpertWeights(fake, fake, fake, shared_gate=fake, shared_up=fake, shared_down=fake)
+    # NULL x
+    st = lib.moe_route(ctypes.byref(cfg), T, None, fake, None, fake, fake, fake, need, None)
+    assert st == -1 and b"x must not be NULL" in lib.moe_last_error()
+    # misaligned router weight
+    st = lib.moe_route(ctypes.byref(cfg), T, fake, fake + 4, None, fake, fake, fake, need, None)
+    assert st == -3
+    # workspace too small / NULL / misaligned
+    assert lib.moe_route(ctypes.byref(cfg), T, fake, fake, None, fake, fake, fake, need - 1, None) == -4
+    assert lib.moe_route(ctypes.byref(cfg), T, fake, fake, None, fake, fake, None, need, None) == -4
+    assert lib.moe_route(ctypes.byref(cfg), T, fake, fake, None, fake, fake, fake + 16, need, None) == -3
+    # dispatch / ffn / combine / forward
+    assert lib.moe_dispatch(ctypes.byref(cfg), T, fake, None, fake, fake, fake, fake, need, None) == -1
+    no_shared = moe.MoEExpertWeights(fake, fake, fake)
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), T, fake, fake, fake, ctypes.byref(no_shared.struct), fake,
+                              fake, need, None) == -1
+    assert lib.moe_combine(ctypes.byref(cfg), T, fake, fake, None, fake, None) == -1
+    assert lib.moe_forward(ctypes.byref(cfg), T, fake, fake, None, ctypes.byref(w.struct), None, None, None, None,
+                           fake, need, None) == -1
+    # MXFP4 needs scales
+    cfg4 = cfg_for(CONFIGS["mxfp4"])
+    assert lib.moe_expert_ffn(ctypes.byref(cfg4), T, fake, fake, fake, ctypes.byref(w.struct), fake, fake,
+                              moe.moe_workspace_size(cfg4, T), None) == -1
+    assert b"scale" in lib.moe_last_error()
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = cfg_for(CONFIGS["decode"])
+    lib = moe.load_library()
+    w = moe.MoEExpertWeights(None, None, None)
+    # T = 0 returns before looking at any pointer or touching the GPU
+    assert lib.moe_forward(ctypes.byref(cfg), 0, None, None, None, ctypes.byref(w.struct), None, None, None, None,
+                           None, 0, None) == 0
+    assert lib.moe_route(ctypes.byref(cfg), 0, None, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_combine(ctypes.byref(cfg), 0, None, None, None, None, None) == 0

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP library (called through the C ABI) against the CPU oracle on seeded
+synthetic inputs.
+
+Bar: expert indices and per-expert counts bit-exact except on tokens whose routing score gap is
+below 1e-6 (counted and reported); outputs within max|err| <= 2e-2 * RMS(oracle output) for
+bf16 expert weights and 5e-2 * RMS for MXFP4 (against the oracle on the decoded weights)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import CONFIGS, gen_experts, quantise_mxfp4
+
+from moe_case import (DeviceCase, compare_routing, expected_counts, host_case, oracle_forward, oracle_route, rms,
+                      to_bits, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_MXFP4 = 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_forward(c, rows=None, tol=TOL_BF16, dev=None):
+    """Run moe_forward on the whole case; compare routing for every token and the output on
+    `rows` (all tokens if None)."""
+    s = c.shape
+    say(f"[gpu] moe_forward {s.name} T={s.T} H={s.H} E={s.E} fmt={s.weight_format} seed={c.seed}")
+    dev = dev or DeviceCase(c)
+    out, idx, w, cnt = dev.forward()
+    out_b = oracle.bf16_to_f64(to_bits(out))
+    idx, w, cnt = idx.cpu().numpy(), w.cpu().numpy(), cnt.cpu().numpy()
+    r_all = oracle_route(c)
+    n_tie, n_mis = compare_routing(r_all, idx, w)
+    say(f"      near-ties {n_tie} (routing differs on {n_mis} of them)")
+    np.testing.assert_array_equal(cnt, expected_counts(r_all, idx, s.E, s.T, s.num_shared_experts))
+    ref, r = oracle_forward(c, rows)
+    got = out_b if rows is None else out_b[rows]
+    keep = ~r.near_tie
+    err = np.abs(got - ref)[keep]
+    bound = tol * rms(ref)
+    say(f"      max|err| = {err.max():.3e}, RMS(ref) = {rms(ref):.3e}, ratio {err.max() / rms(ref):.3e} (bar {tol})")
+    assert err.max() <= bound
+    return dev, out
+
+
+# ----------------------------------------------------------------------------------
+# tiny layer: every token, every stage
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [32, 1, 17, 63, 64, 65, 200, 1000])
+def test_forward_tiny(T):
+    check_forward(host_case(CONFIGS["tiny"], seed=0, T=T))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_forward_tiny_seeds(seed):
+    check_forward(host_case(CONFIGS["tiny"], seed=seed, T=96))
+
+
+def test_forward_tiny_clamped():
+    c = host_case(CONFIGS["tiny"].with_(swiglu_limit=0.002, shared_swiglu_limit=0.003), seed=5, T=77)
+    check_forward(c)
+
+
+def test_forward_tiny_no_shared_no_norm():
+    c = host_case(CONFIGS["tiny"].with_(num_shared_experts=0, norm_topk_prob=False), seed=6, T=50)
+    check_forward(c)
+
+
+def test_stages_tiny():
+    """Each entry point alone, fed the oracle's outputs of the previous stage."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    c = host_case(CONFIGS["tiny"], seed=7, T=130)
+    s = c.shape
+    T, K, E, H = s.T, s.K, s.E, s.H
+    dev = DeviceCase(c)
+    say("[gpu] moe_route tiny T=130")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    moe.moe_route(dev.cfg, T, dev.x, dev.router_w, dev.bias, idx, w, dev.ws)
+    torch.cuda.synchronize()
+    r = oracle_route(c)
+    compare_routing(r, idx.cpu().numpy(), w.cpu().numpy())
+
+    say("[gpu] moe_dispatch tiny T=130 (oracle routing in)")
+    d = oracle.dispatch(r.topk_idx, E, 1)
+    idx_in = to_dev(r.topk_idx.astype(np.int32))
+    counts = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 2, dtype=torch.int32, device="cuda")
+    sorted_token = torch.empty(T * K + T, dtype=torch.int32, device="cuda")
+    inv = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(dev.cfg, T, idx_in, counts, offsets, sorted_token, inv, dev.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts.cpu().numpy(), d.counts)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), d.offsets)
+    np.testing.assert_array_equal(sorted_token.cpu().numpy(), d.sorted_token)
+    np.testing.assert_array_equal(inv.cpu().numpy(), d.inv_perm)
+
+    say("[gpu] moe_expert_ffn tiny T=130 (oracle dispatch in)")
+    y = torch.empty((T * K + T, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(dev.cfg, T, dev.x, to_dev(d.offsets.astype(np.int32)), to_dev(d.sorted_token.astype(np.int32)),
+                       dev.weights, y, dev.ws)
+    torch.cuda.synchronize()
+    x = oracle.bf16_to_f64(c.x)
+    y_ref = np.zeros((T * K + T, H))
+    for e in range(E + 1):
+        p0, p1 = d.offsets[e], d.offsets[e + 1]
+        if p1 > p0:
+            wts = c.expert_f64(e) if e < E else c.shared_f64()
+            y_ref[p0:p1] = oracle.expert_forward(x[d.sorted_token[p0:p1]], *wts)
+    y_got = y.cpu().numpy().astype(np.float64)
+    assert np.abs(y_got - y_ref).max() <= TOL_BF16 * rms(y_ref)
+
+    say("[gpu] moe_combine tiny T=130 (oracle expert outputs in, rounded to fp32)")
+    y32 = y_ref.astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(dev.cfg, T, to_dev(y32), to_dev(d.inv_perm.astype(np.int32)),
+                    to_dev(r.topk_w.astype(np.float32)), out)
+    torch.cuda.synchronize()
+    yb = y32.astype(np.float64)
+    ref = (r.topk_w[:, :, None] * yb[d.inv_perm]).sum(1) + yb[T * K:]
+    got = oracle.bf16_to_f64(to_bits(out))
+    # only fp32 accumulation and the final bf16 rounding separate the two
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * rms(ref))
+
+
+def test_determinism_tiny():
+    import torch
+    c = host_case(CONFIGS["tiny"], seed=8, T=300)
+    dev = DeviceCase(c)
+    say("[gpu] moe_forward twice, tiny T=300")
+    a = [t.clone() for t in dev.forward()]
+    b = dev.forward()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
+# ----------------------------------------------------------------------------------
+# adversarial fixtures (tiny layer)
+# ----------------------------------------------------------------------------------
+def test_fixture_negative_biased_scores():
+    # every biased score below zero: experts of dropped groups must stay excluded
+    s = CONFIGS["tiny"]
+    c = host_case(s, seed=9, T=64, bias=np.full(s.E, -2.0, np.float32))
+    check_forward(c)
+
+
+def test_fixture_exact_ties_lower_index_wins():
+    # experts 2j and 2j+1 get identical router rows and biases, so their scores are bitwise
+    # equal on both sides; whenever only one of a pair is chosen it must be the lower one.
+    # K = 7 is odd, so the pair at the K-th place is always split.
+    s = CONFIGS["tiny"].with_(num_experts_per_tok=7)
+    base = host_case(s, seed=10, T=64)
+    rw = np.repeat(base.router_w[::2], 2, axis=0)
+    bias = np.repeat(base.bias[::2], 2)
+    c = host_case(s, seed=10, T=64, router_w=rw, bias=bias)
+    say("[gpu] moe_forward tiny T=64 with tied expert pairs")
+    dev = DeviceCase(c)
+    out, idx, w, cnt = dev.forward()
+    idx = idx.cpu().numpy()
+    r = oracle_route(c)
+    compare_routing(r, idx, w.cpu().numpy())
+    for t in range(c.shape.T):
+        chosen = set(idx[t].tolist())
+        for e in chosen:
+            if e % 2 == 1:
+                assert e - 1 in chosen, (t, sorted(chosen))
+    # the rule was exercised: some chosen expert's partner was left out
+    assert any(sum((e ^ 1) in set(row.tolist()) for e in row) < len(row) for row in idx)
+
+
+def test_fixture_all_tokens_same_experts():
+    # a huge bias on 8 experts of one group sends every token to them (count = T each)
+    s = CONFIGS["tiny"]
+    bias = np.zeros(s.E, np.float32)
+    hot = [8, 9, 10, 11, 12, 13, 14, 15]
+    bias[hot] = 5.0
+    c = host_case(s, seed=11, T=517, bias=bias)
+    dev, _ = check_forward(c)
+    out, idx, w, cnt = dev.forward()
+    cnt = cnt.cpu().numpy()
+    assert (cnt[hot] == 517).all() and cnt[:s.E].sum() == 517 * 8
+
+
+def test_fixture_identical_experts():
+    # all routed experts equal: out = 2.5 * FFN(x) + shared(x) whatever the routing
+    s = CONFIGS["tiny"]
+    ex = gen_experts(s, seed=12)
+    for k in ("gate", "up", "down"):
+        ex[k][:] = ex[k][3]
+    c = host_case(s, seed=12, T=90, experts=ex)
+    dev, out = check_forward(c)
+    x = oracle.bf16_to_f64(c.x)
+    want = 2.5 * oracle.expert_forward(x, *c.expert_f64(0)) + oracle.expert_forward(x, *c.shared_f64())
+    got = oracle.bf16_to_f64(to_bits(out))
+    assert np.abs(got - want).max() <= TOL_BF16 * rms(want)
+
+
+def test_fixture_no_bias_pointer():
+    import torch
+    s = CONFIGS["tiny"]
+    c = host_case(s, seed=13, T=40, bias=np.zeros(s.E, np.float32))
+    dev = DeviceCase(c)
+    a = dev.forward(bias=True)
+    b = dev.forward(bias=False)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ----------------------------------------------------------------------------------
+# full-size layer (H 2560, 512 experts, intermediate 768)
+# ----------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def full_experts():
+    say("[host] drawing the 512 full-size experts (bf16)")
+    return gen_experts(CONFIGS["decode"], seed=0)
+
+
+@pytest.mark.slow
+def test_forward_decode_full(full_experts):
+    check_forward(host_case(CONFIGS["decode"], seed=0, experts=full_experts))
+
+
+def _sample_rows(T, n=24):
+    rng = np.random.default_rng(T)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+
+
+@pytest.mark.slow
+def test_forward_prefill_full(full_experts):
+    c = host_case(CONFIGS["prefill"], seed=0, experts=full_experts)
+    check_forward(c, rows=_sample_rows(c.shape.T))
+
+
+@pytest.mark.slow
+def test_forward_skewed_full(full_experts):
+    c = host_case(CONFIGS["skewed"], seed=0, experts=full_experts)
+    r = oracle_route(c)
+    cnt = np.sort(r.counts)[::-1]
+    top = cnt[: c.shape.E // 10].sum() / cnt.sum()
+    say(f"      skew: top-10% experts take {top:.3f} of assignments; {(cnt > 0).sum()} experts touched")
+    assert top > 0.5
+    check_forward(c, rows=_sample_rows(c.shape.T))
+
+
+@pytest.mark.slow
+def test_forward_mxfp4_full(full_experts):
+    from concurrent.futures import ThreadPoolExecutor
+    s = CONFIGS["mxfp4"]
+    E, I, H = s.E, s.I, s.H
+    ex = dict(gate_q=np.empty((E, I, H // 2), np.uint8), gate_s=np.empty((E, I, H // 32), np.uint8),
+              up_q=np.empty((E, I, H // 2), np.uint8), up_s=np.empty((E, I, H // 32), np.uint8),
+              down_q=np.empty((E, H, I // 2), np.uint8), down_s=np.empty((E, H, I // 32), np.uint8))
+
+    def q(e):
+        for k in ("gate", "up", "down"):
+            ex[k + "_q"][e], ex[k + "_s"][e] = quantise_mxfp4(full_experts[k][e])
+    say("[host] quantising the 512 experts to MXFP4")
+    with ThreadPoolExecutor(16) as pool:
+        list(pool.map(q, range(E)))
+    c = host_case(s, seed=0, experts=ex)
+    check_forward(c, rows=_sample_rows(s.T), tol=TOL_MXFP4)
