@@ -2,13 +2,15 @@
 // FFNs can run as a grouped GEMM over contiguous row blocks (the routing walk-through page,
 // lqnn.cn, section 三.2, ends with 8 experts per token; each expert then serves its tokens).
 //
-// Deterministic and atomic-order independent:
-//   1. mark     one bit per (expert, token) in a bitmap [E][ceil(T/32)] (atomicOr only sets
-//               bits, so the result does not depend on the order of the atomics);
-//   2. count    one wave per expert: popcount of its bitmap row -> counts[e];
-//   3. scan     one wave: exclusive prefix sum of counts -> offsets;
-//   4. scatter  one wave per expert walks its row in ascending token order and writes
-//               sorted_token and inv_perm; the shared expert's block is the identity.
+// Deterministic and independent of the order of atomics:
+//   1. mark     one bit per (expert, token) in a bitmap [E][ceil(T/32)] and a histogram of
+//               expert counts (atomicOr / atomicAdd on integers: the final values do not
+//               depend on their order).  The fused forward does this inside the router's
+//               top-k kernel and clears the bitmap inside the router's logits kernel.
+//   2. finish   one wave per expert: its offset is the sum of the counts before it; it walks
+//               its bitmap row in ascending token order and writes sorted_token and
+//               inv_perm.  One more wave writes the offsets, the shared expert's identity
+//               block and, for the fused forward, the expert FFN's tile prefix.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -21,72 +23,89 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) 
 }
 
 __global__ void dispatch_mark_kernel(const int32_t* __restrict__ topk_idx, int T, int K, int E, int words,
-                                     uint32_t* __restrict__ bitmap, int32_t* __restrict__ inv_perm) {
+                                     uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts,
+                                     int32_t* __restrict__ inv_perm) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)T * K) return;
   const int e = topk_idx[i];
   const int t = (int)(i / K);
-  if (e >= 0 && e < E)
+  if (e >= 0 && e < E) {
     atomicOr(&bitmap[(size_t)e * words + (t >> 5)], 1u << (t & 31));
-  else
+    atomicAdd(&counts[e], 1);
+  } else {
     inv_perm[i] = -1;  // ignored pair
+  }
 }
 
-// one wave per expert (plus one wave that writes the shared expert's count)
-__global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __restrict__ bitmap, int E, int words,
-                                                             int T, int S, int32_t* __restrict__ counts) {
+// sum of v[0 .. n) over one wave (lane-strided)
+__device__ __forceinline__ int wave_sum_prefix(const int32_t* __restrict__ v, int n, int lane) {
+  int c = 0;
+  for (int i = lane; i < n; i += WAVE) c += v[i];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, WAVE);
+  return c;
+}
+
+// Waves 0..E-1: expert e.  Wave E: offsets, counts_out (a copy of the histogram plus the
+// shared expert's T*S), the shared expert's identity block and (if tile_prefix) the tile
+// prefix of the E + S experts for tiles of bm positions.
+__global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __restrict__ bitmap,
+                                                              const int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ counts_out,
+                                                              const int32_t* __restrict__ topk_idx, int T, int K,
+                                                              int E, int words, int S,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_token,
+                                                              int32_t* __restrict__ inv_perm,
+                                                              int32_t* __restrict__ tile_prefix, int bm) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e > E) return;
   if (e == E) {
-    if (lane == 0) counts[E] = T * S;
+    // exclusive scan of counts[0..E) plus the shared expert
+    const int per = (E + WAVE - 1) / WAVE;
+    const int b = lane * per, en = min(E, b + per);
+    int sum = 0, tsum = 0;
+    for (int i = b; i < en; ++i) {
+      sum += counts[i];
+      if (tile_prefix) tsum += (counts[i] + bm - 1) / bm;
+    }
+    int incl = sum, tincl = tsum;
+#pragma unroll
+    for (int m = 1; m < WAVE; m <<= 1) {
+      int o = __shfl_up(incl, m, WAVE), to = __shfl_up(tincl, m, WAVE);
+      if (lane >= m) {
+        incl += o;
+        tincl += to;
+      }
+    }
+    int run = incl - sum, trun = tincl - tsum;
+    for (int i = b; i < en; ++i) {
+      offsets[i] = run;
+      counts_out[i] = counts[i];
+      run += counts[i];
+      if (tile_prefix) {
+        tile_prefix[i] = trun;
+        trun += (counts[i] + bm - 1) / bm;
+      }
+    }
+    const int routed = __shfl(incl, WAVE - 1, WAVE);
+    const int trouted = __shfl(tincl, WAVE - 1, WAVE);
+    if (lane == 0) {
+      counts_out[E] = T * S;
+      offsets[E] = routed;
+      offsets[E + 1] = routed + T * S;
+      if (tile_prefix) {
+        tile_prefix[E] = trouted;
+        tile_prefix[E + 1] = trouted + (S ? (T + bm - 1) / bm : 0);
+      }
+    }
+    if (S)
+      for (int t = lane; t < T; t += WAVE) sorted_token[routed + t] = t;
     return;
   }
-  const uint32_t* row = bitmap + (size_t)e * words;
-  int c = 0;
-  for (int w = lane; w < words; w += WAVE) c += __popc(row[w]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, WAVE);
-  if (lane == 0) counts[e] = c;
-}
-
-// single wave: offsets[0] = 0, offsets[i+1] = offsets[i] + counts[i] for i < n
-__global__ __launch_bounds__(64) void exclusive_scan_kernel(const int32_t* __restrict__ counts, int n,
-                                                            int32_t* __restrict__ offsets) {
-  const int lane = threadIdx.x;
-  const int per = (n + WAVE - 1) / WAVE;
-  const int b = lane * per, e = min(n, b + per);
-  int sum = 0;
-  for (int i = b; i < e; ++i) sum += counts[i];
-  int incl = sum;
-#pragma unroll
-  for (int m = 1; m < WAVE; m <<= 1) {
-    int o = __shfl_up(incl, m, WAVE);
-    if (lane >= m) incl += o;
-  }
-  int run = incl - sum;
-  if (lane == 0) offsets[0] = 0;
-  for (int i = b; i < e; ++i) {
-    run += counts[i];
-    offsets[i + 1] = run;
-  }
-}
-
-// one wave per expert; expert E (if S) writes the identity block
-__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const uint32_t* __restrict__ bitmap,
-                                                               const int32_t* __restrict__ offsets,
-                                                               const int32_t* __restrict__ topk_idx, int T, int K,
-                                                               int E, int words, int S,
-                                                               int32_t* __restrict__ sorted_token,
-                                                               int32_t* __restrict__ inv_perm) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e > E || (e == E && !S)) return;
-  int base = offsets[e];
-  if (e == E) {
-    for (int t = lane; t < T; t += WAVE) sorted_token[base + t] = t;
-    return;
-  }
+  int base = wave_sum_prefix(counts, e, lane);
+  const int end = base + counts[e];
   const uint32_t* row = bitmap + (size_t)e * words;
   for (int w0 = 0; w0 < words; w0 += WAVE) {
     const int w = w0 + lane;
@@ -111,31 +130,35 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const uint32_t* _
     }
     base += __shfl(incl, WAVE - 1, WAVE);
   }
+  // a token listing the same expert twice is counted twice but has one bit: mark the
+  // positions that no token fills (the expert FFN skips negative tokens)
+  for (int p = base + lane; p < end; p += WAVE) sorted_token[p] = -1;
 }
 
 }  // namespace
 
 size_t dispatch_bitmap_words(int64_t T, int E) { return (size_t)E * (size_t)((T + 31) / 32); }
 
+
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, uint32_t* bitmap, int32_t* counts,
-                           int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, hipStream_t s, Tracer* tr) {
+                           int32_t* counts_out, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, bool marked,
+                           int32_t* tile_prefix, int bm, hipStream_t s, Tracer* tr) {
   const int words = (T + 31) / 32;
-  const size_t nbits = (size_t)E * words;
-  int zb = (int)std::min<size_t>((nbits + 255) / 256, 1024);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(zb), dim3(256), 0, s, bitmap, nbits, 0u);
-  if (tr) tr->mark("dispatch_clear", s);
-  const int64_t pairs = (int64_t)T * K;
-  hipLaunchKernelGGL(dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, topk_idx, T, K, E,
-                     words, bitmap, inv_perm);
-  if (tr) tr->mark("dispatch_mark", s);
+  if (!marked) {
+    const size_t nbits = (size_t)E * words;
+    int zb = (int)std::min<size_t>((nbits + 255) / 256, 1024);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(zb), dim3(256), 0, s, bitmap, nbits, 0u);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, s, (uint32_t*)counts, (size_t)E, 0u);
+    if (tr) tr->mark("dispatch_clear", s);
+    const int64_t pairs = (int64_t)T * K;
+    hipLaunchKernelGGL(dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, topk_idx, T, K,
+                       E, words, bitmap, counts, inv_perm);
+    if (tr) tr->mark("dispatch_mark", s);
+  }
   const int eb = (E + 1 + 3) / 4;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(eb), dim3(256), 0, s, bitmap, E, words, T, S, counts);
-  if (tr) tr->mark("dispatch_count", s);
-  hipLaunchKernelGGL(exclusive_scan_kernel, dim3(1), dim3(64), 0, s, counts, E + 1, offsets);
-  if (tr) tr->mark("dispatch_scan", s);
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(eb), dim3(256), 0, s, bitmap, offsets, topk_idx, T, K, E, words, S,
-                     sorted_token, inv_perm);
-  if (tr) tr->mark("dispatch_scatter", s);
+  hipLaunchKernelGGL(dispatch_finish_kernel, dim3(eb), dim3(256), 0, s, bitmap, counts, counts_out, topk_idx, T, K, E,
+                     words, S, offsets, sorted_token, inv_perm, tile_prefix, bm);
+  if (tr) tr->mark("dispatch_finish", s);
   return hipGetLastError();
 }
 

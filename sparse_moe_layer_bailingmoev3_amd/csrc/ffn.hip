@@ -51,6 +51,8 @@ struct FfnArgs {
   int K;                        // reduction length
   int N;                        // output columns per expert
   int nrb;                      // row blocks per expert (N / rows per workgroup)
+  int rbw;                      // row blocks one workgroup streams back to back
+  int ngroups;                  // ceil(nrb / rbw): row-block groups per tile
   float limit, shared_limit;
 };
 
@@ -87,13 +89,22 @@ struct WStage {
   uint32_t sc[NMAT][RF];
 };
 
-template <int NW, int RF, int MF, int MODE, int KS, bool FP4>
-__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nrows, int rb, uint16_t* lds) {
+template <int NTP, int CPT>
+struct TStage {
+  u32x4 t[NTP][CPT];
+};
+
+// One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
+// tile) are issued while step s computes, all in one batch, so that waiting for the token
+// tile of the next step (loads complete in issue order) never waits for younger weights.
+template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nrows, int rb0, int nrb_here,
+                                         uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;  // token planes (h hi and lo for down)
   constexpr int BM = MF * 16;
   constexpr int SUB = KS / 32;       // MFMA sub-steps per step
-  constexpr int LROW = KS + 8;       // LDS row stride (bf16), 16-byte pad against bank conflicts
+  constexpr int LROW = KS + 16;      // LDS row stride (bf16); the 32-byte pad measured fewest bank conflicts
   constexpr int NTH = NW * 64;
   constexpr int CHUNKS = BM * KS / 8;  // 16-byte pieces of one token plane per step
   constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
@@ -103,7 +114,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int K = a.K, N = a.N;
-  const int nsteps = K / KS;
+  const int nsteps = K / KS;                 // k-steps per row block
+  const int total_steps = nsteps * nrb_here;  // the pipeline runs through all row blocks
   const bool shared = e == a.E;
   const int pos0 = a.offsets[e] + m0;
 
@@ -131,8 +143,11 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
     }
   }
 
-  // weight rows of this lane
-  const int nbase = rb * ROWS + wave * RF * 16;
+  // weight rows of this lane.  bf16: sub-step s of a step reads k = 32s + 8q .. +7, so
+  // one load instruction covers 64 contiguous bytes of each of the 16 rows.  MXFP4: lane
+  // group q owns the 32-value block q of the step (16 bytes of codes, one scale byte) and
+  // sub-step s uses its codes 8s .. 8s+7.
+  const int nbase = rb0 * ROWS + wave * RF * 16;
   const uint16_t* wp[NMAT][RF];
   const uint8_t* wq[NMAT][RF];
   const uint8_t* wsc[NMAT][RF];
@@ -150,7 +165,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
       } else {
         const uint16_t* base = shared ? (const uint16_t*)(m == 0 ? a.sw0 : a.sw1)
                                       : (const uint16_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * K;
-        wp[m][f] = base + row * K + q * (KS / 4);
+        wp[m][f] = base + row * K + q * 8;
         wq[m][f] = nullptr;
         wsc[m][f] = nullptr;
       }
@@ -164,44 +179,48 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 treg[NTP][CPT];
-  auto load_t = [&](int step) {
+  auto load_t = [&](TStage<NTP, CPT>& ts, int step) {
+    const int ks = step % nsteps;
 #pragma unroll
     for (int p = 0; p < NTP; ++p)
 #pragma unroll
       for (int i = 0; i < CPT; ++i)
-        treg[p][i] = tsrc[p][i] ? *(const u32x4*)(tsrc[p][i] + step * KS) : u32x4{0u, 0u, 0u, 0u};
+        ts.t[p][i] = tsrc[p][i] ? *(const u32x4*)(tsrc[p][i] + ks * KS) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto store_t = [&](int buf) {
+  auto store_t = [&](const TStage<NTP, CPT>& ts, int buf) {
 #pragma unroll
     for (int p = 0; p < NTP; ++p)
 #pragma unroll
       for (int i = 0; i < CPT; ++i)
-        if (tdst[i] >= 0) *(u32x4*)(lds + (buf * NTP + p) * BM * LROW + tdst[i]) = treg[p][i];
+        if (tdst[i] >= 0) *(u32x4*)(lds + (buf * NTP + p) * BM * LROW + tdst[i]) = ts.t[p][i];
   };
+  // (plain loads: nontemporal loads measured ~25% slower on these streams)
   auto load_w = [&](WStage<NMAT, RF, WREGS>& st, int step) {
+    const int rbi = step / nsteps, ks = step - rbi * nsteps;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
         if constexpr (FP4) {
-          st.w[m][f][0] = *(const u32x4*)(wq[m][f] + (size_t)step * (KS / 2));
-          st.sc[m][f] = wsc[m][f][(size_t)step * (KS / 32)];
+          st.w[m][f][0] = *(const u32x4*)(wq[m][f] + (size_t)rbi * ROWS * (K / 2) + (size_t)ks * (KS / 2));
+          st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32)];
         } else {
 #pragma unroll
-          for (int s = 0; s < WREGS; ++s) st.w[m][f][s] = *(const u32x4*)(wp[m][f] + (size_t)step * KS + s * 8);
+          for (int s = 0; s < WREGS; ++s)
+            st.w[m][f][s] = *(const u32x4*)(wp[m][f] + (size_t)rbi * ROWS * K + (size_t)ks * KS + s * 32);
         }
       }
   };
   auto compute = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
-    const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW + q * (KS / 4);
+    const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
+      const int col = FP4 ? q * 32 + s * 8 : s * 32 + q * 8;
       u32x4 tf[NTP][MF];
 #pragma unroll
       for (int p = 0; p < NTP; ++p)
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf) tf[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + s * 8);
+        for (int mf = 0; mf < MF; ++mf) tf[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -220,76 +239,89 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
     }
   };
 
-  WStage<NMAT, RF, WREGS> sa, sb;
-  load_t(0);
-  load_w(sa, 0);
-  store_t(0);
-  if (nsteps > 1) {
-    load_t(1);
-    load_w(sb, 1);
-  }
-  block_sync_lds();
-  for (int s = 0; s < nsteps; s += 2) {
-    compute(sa, 0);
-    if (s + 1 < nsteps) store_t(1);
-    if (s + 2 < nsteps) {
-      load_t(s + 2);
-      load_w(sa, s + 2);
-    }
-    block_sync_lds();
-    if (s + 1 >= nsteps) break;
-    compute(sb, 1);
-    if (s + 2 < nsteps) store_t(0);
-    if (s + 3 < nsteps) {
-      load_t(s + 3);
-      load_w(sb, s + 3);
-    }
-    block_sync_lds();
-  }
-
-  // epilogue: lane holds token r16 of each fragment and rows 4q .. 4q+3 of each 16-row block
+  // epilogue of one row block: lane holds token r16 of each fragment and rows 4q .. 4q+3 of
+  // each 16-row block
   const float limit = shared ? a.shared_limit : a.limit;
+  auto epilogue = [&](int rbi) {
+    const int ncol = nbase + rbi * ROWS + 4 * q;
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    const int j = mf * 16 + r16;
-    if (j >= nrows) continue;
-    const size_t obase = (size_t)(pos0 + j) * N + nbase + 4 * q;
+    for (int mf = 0; mf < MF; ++mf) {
+      const int j = mf * 16 + r16;
+      if (j < nrows) {
+        const size_t obase = (size_t)(pos0 + j) * N + ncol;
 #pragma unroll
-    for (int f = 0; f < RF; ++f) {
-      if (MODE == MODE_GATEUP) {
-        float hv[4], lv[4];
+        for (int f = 0; f < RF; ++f) {
+          if (MODE == MODE_GATEUP) {
+            float hv[4], lv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float g = acc[0][f][mf][r], u = acc[NMAT - 1][f][mf][r];
-          float h = g / (1.0f + __expf(-g)) * u;
-          if (limit > 0.f) h = fminf(fmaxf(h, -limit), limit);
-          hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
-          lv[r] = h - hv[r];  // exact in fp32
+            for (int r = 0; r < 4; ++r) {
+              const float g = acc[0][f][mf][r], u = acc[NMAT - 1][f][mf][r];
+              float h = g / (1.0f + __expf(-g)) * u;
+              if (limit > 0.f) h = fminf(fmaxf(h, -limit), limit);
+              hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
+              lv[r] = h - hv[r];  // exact in fp32
+            }
+            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          } else {
+            *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][mf];
+          }
         }
-        *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-        *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
-      } else {
-        *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][mf];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  WStage<NMAT, RF, WREGS> ws[D];
+  TStage<NTP, CPT> ts[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (j < total_steps) {
+      load_t(ts[j], j);
+      load_w(ws[j], j);
+    }
+  }
+  store_t(ts[0], 0);
+  block_sync_lds();
+  for (int s0 = 0; s0 < total_steps; s0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int s = s0 + j;
+      if (s < total_steps) {
+        if (s + 1 < total_steps) store_t(ts[(j + 1) % D], (s + 1) & 1);
+        compute(ws[j], s & 1);
+        if (s + D < total_steps) {
+          load_t(ts[j], s + D);
+          load_w(ws[j], s + D);
+        }
+        if ((s + 1) % nsteps == 0) epilogue(s / nsteps);
+        block_sync_lds();
       }
     }
   }
 }
 
-template <int NW, int RF, int MF, int MODE, int FMT>
+template <int NW, int RF, int MF, int D, int MODE, int FMT>
 __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr int KS = FMT == FMT_MXFP4 ? 128 : 64;
   constexpr int BM = MF * 16;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
-  __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 8)];
+  __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 16)];
 
   // device work list: work id -> (tile, row block); tiles of one XCD are consecutive
-  const int total = a.tile_prefix[a.E + a.S] * a.nrb;
+  const int total = a.tile_prefix[a.E + a.S] * a.ngroups;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
   if (slot >= per_xcd) return;
   const int w = (blockIdx.x & 7) * per_xcd + slot;
   if (w >= total) return;
-  const int tile = w / a.nrb, rb = w - tile * a.nrb;
+  const int tile = w / a.ngroups, grp = w - tile * a.ngroups;
+  const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
   int lo = 0, hi = a.E + a.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -301,11 +333,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int nrows = min(BM, cnt - m0);
   if constexpr (FMT == FMT_MXFP4) {
     if (e < a.E) {
-      ffn_tile<NW, RF, MF, MODE, KS, true>(a, e, m0, nrows, rb, lds);
+      ffn_tile<NW, RF, MF, D, MODE, KS, true>(a, e, m0, nrows, rb0, nrb_here, lds);
       return;
     }
   }
-  ffn_tile<NW, RF, MF, MODE, KS, false>(a, e, m0, nrows, rb, lds);
+  ffn_tile<NW, RF, MF, D, MODE, KS, false>(a, e, m0, nrows, rb0, nrb_here, lds);
 }
 
 // single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan
@@ -330,14 +362,22 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
   }
 }
 
-constexpr int FFN_NW = 4, FFN_RF = 2, FFN_ROWS = FFN_NW * FFN_RF * 16;
+// rows of weights per workgroup (NW * RF * 16) is 128 in every configuration
+constexpr int FFN_ROWS = 128;
+template <int MF, int FMT> struct FfnCfg;
+template <int FMT> struct FfnCfg<1, FMT> { static constexpr int NW = 4, RF = 2, D = FMT == FMT_MXFP4 ? 3 : 4; };
+template <int FMT> struct FfnCfg<2, FMT> { static constexpr int NW = 4, RF = 2, D = FMT == FMT_MXFP4 ? 3 : 4; };
+template <int FMT> struct FfnCfg<4, FMT> { static constexpr int NW = 8, RF = 1, D = FMT == FMT_MXFP4 ? 2 : 4; };
+template <int FMT> struct FfnCfg<8, FMT> { static constexpr int NW = 8, RF = 1, D = FMT == FMT_MXFP4 ? 2 : 4; };
 
 template <int MF, int MODE, int FMT>
 hipError_t launch_one(const FfnArgs& a, int64_t max_tiles, hipStream_t s, Tracer* tr) {
-  int64_t work = max_tiles * a.nrb;
+  using C = FfnCfg<MF, FMT>;
+  static_assert(C::NW * C::RF * 16 == FFN_ROWS, "rows per workgroup");
+  int64_t work = max_tiles * a.ngroups;
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_kernel<FFN_NW, FFN_RF, MF, MODE, FMT>), dim3((unsigned)grid), dim3(FFN_NW * 64), 0, s, a);
+  hipLaunchKernelGGL((ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT>), dim3((unsigned)grid), dim3(C::NW * 64), 0, s, a);
   hipError_t err = hipGetLastError();
   if (tr) tr->mark(MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
   return err;
@@ -363,6 +403,10 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S) {
   const double avg = (double)T * K / E;  // routed tokens per expert on average
   p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : 8;
   p.bm = 16 * p.mf;
+  // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
+  // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
+  p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
+  p.rbw_down = p.mf >= 4 ? 5 : 4;
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
   return p;
@@ -371,10 +415,13 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S) {
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                              int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
                              float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
-                             hipStream_t s, Tracer* tr) {
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
-  hipError_t err = hipGetLastError();
-  if (tr) tr->mark("expert_tiles", s);
+                             bool tiles_ready, hipStream_t s, Tracer* tr) {
+  hipError_t err = hipSuccess;
+  if (!tiles_ready) {
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
+    err = hipGetLastError();
+    if (tr) tr->mark("expert_tiles", s);
+  }
   if (err != hipSuccess) return err;
 
   FfnArgs gu{};
@@ -382,6 +429,8 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   gu.w0 = w.gate; gu.w1 = w.up; gu.s0 = w.gate_scale; gu.s1 = w.up_scale;
   gu.sw0 = w.sh_gate; gu.sw1 = w.sh_up; gu.out = h_hi; gu.out_lo = h_lo;
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I; gu.nrb = I / FFN_ROWS;
+  gu.rbw = std::min(gu.nrb, p.rbw_gate_up);
+  gu.ngroups = (gu.nrb + gu.rbw - 1) / gu.rbw;
   gu.limit = limit; gu.shared_limit = shared_limit;
 
   FfnArgs dn = gu;
@@ -389,6 +438,8 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   dn.w0 = w.down; dn.w1 = nullptr; dn.s0 = w.down_scale; dn.s1 = nullptr;
   dn.sw0 = w.sh_down; dn.sw1 = nullptr; dn.out = y;
   dn.K = I; dn.N = H; dn.nrb = H / FFN_ROWS;
+  dn.rbw = std::min(dn.nrb, p.rbw_down);
+  dn.ngroups = (dn.nrb + dn.rbw - 1) / dn.rbw;
 
   switch (p.mf) {
     case 1: return launch_mf<1>(gu, dn, w.fmt, p.max_tiles, s, tr);

@@ -7,7 +7,7 @@
 #include <cmath>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {
@@ -81,7 +81,7 @@ moe_status_t validate_config(const moe_config_t* c, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t partial, bitmap, counts, offsets, tile_prefix, topk_idx, topk_w, sorted_token, inv_perm, h_hi, h_lo, y,
+  size_t partial, bitmap, counts, counts_out, offsets, tile_prefix, topk_idx, topk_w, sorted_token, inv_perm, h_hi, h_lo, y,
       total;
 };
 
@@ -99,6 +99,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.partial = take(moe::router_partial_bytes(T, (int)H, (int)E));
   L.bitmap = take(moe::dispatch_bitmap_words(T, (int)E) * 4);
   L.counts = take((E + 1) * 4);
+  L.counts_out = take((E + 1) * 4);
   L.offsets = take((E + 2) * 4);
   L.tile_prefix = take((E + 2) * 4);
   L.topk_idx = take(T * K * 4);
@@ -150,39 +151,51 @@ moe::FfnWeights ffn_weights(const moe_config_t* c, const moe_expert_weights_t* w
 
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
+// mark: also clear (logits kernel) and fill (top-k kernel) the dispatch bitmap and the
+// expert histogram in the workspace, so moe_dispatch's clear and mark kernels are not needed
 moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const float* rw, const float* bias,
                       int32_t* idx, float* wts, const Layout& L, void* ws, hipStream_t s,
-                      moe::Tracer* tr = nullptr) {
+                      moe::Tracer* tr = nullptr, bool mark = false) {
   moe::RouterPlan p = moe::router_plan(T, c->hidden_size, c->num_experts);
   float* partial = (float*)at(ws, L.partial);
+  uint32_t* bitmap = mark ? (uint32_t*)at(ws, L.bitmap) : nullptr;
+  int32_t* counts = mark ? (int32_t*)at(ws, L.counts) : nullptr;
+  // the bitmap and the counts are adjacent in the layout: one range to clear
+  const int64_t clear_words = (int64_t)(L.counts - L.bitmap) / 4 + c->num_experts;
   hipError_t e = moe::launch_router_logits(p, (const uint16_t*)x, rw, (int)T, c->hidden_size, c->num_experts,
-                                           partial, s, tr);
+                                           partial, bitmap, clear_words, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router logits launch");
   e = moe::launch_router_topk(partial, p.nsplit, (int)T, c->num_experts, bias, c->n_group, c->topk_group,
-                              c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, s, tr);
+                              c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, bitmap,
+                              counts, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router top-k launch");
   return MOE_OK;
 }
 
+// marked: the router already filled the bitmap and the workspace histogram; counts are
+// then copied to `counts` by the finish kernel.  with_tiles: also write the FFN tile prefix.
 moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_token, int32_t* inv_perm, const Layout& L, void* ws, hipStream_t s,
-                         moe::Tracer* tr = nullptr) {
+                         moe::Tracer* tr = nullptr, bool marked = false, bool with_tiles = false) {
+  moe::FfnPlan fp = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts);
+  int32_t* hist = marked ? (int32_t*)at(ws, L.counts) : counts;
   hipError_t e = moe::launch_dispatch(idx, (int)T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
-                                      (uint32_t*)at(ws, L.bitmap), counts, offsets, sorted_token, inv_perm, s, tr);
+                                      (uint32_t*)at(ws, L.bitmap), hist, counts, offsets, sorted_token, inv_perm,
+                                      marked, with_tiles ? (int32_t*)at(ws, L.tile_prefix) : nullptr, fp.bm, s, tr);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
   return MOE_OK;
 }
 
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32_t* offsets,
                     const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
-                    hipStream_t s, moe::Tracer* tr = nullptr) {
+                    hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false) {
   moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts);
   const float lim = c->swiglu_limit > 0 ? c->swiglu_limit : 0.f;
   const float slim = c->shared_swiglu_limit > 0 ? c->shared_swiglu_limit : 0.f;
   hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),
                                         ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
                                         c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
-                                        (uint16_t*)at(ws, L.h_lo), (float*)y, s, tr);
+                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr);
   if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   return MOE_OK;
 }
@@ -310,15 +323,16 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
   hipStream_t s = (hipStream_t)stream;
   int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)at(ws, L.topk_idx);
   float* wts = topk_w_out ? topk_w_out : (float*)at(ws, L.topk_w);
-  int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)at(ws, L.counts);
+  int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)at(ws, L.counts_out);
   int32_t* offsets = (int32_t*)at(ws, L.offsets);
   int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);
   void* y = at(ws, L.y);
   if (tr && tr->events && tr->cap > 0) hipEventRecord(tr->events[0], s);
-  if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr)) != MOE_OK) return st;
-  if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr)) != MOE_OK) return st;
-  if ((st = do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr)) != MOE_OK) return st;
+  if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true)) != MOE_OK) return st;
+  if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
+    return st;
+  if ((st = do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true)) != MOE_OK) return st;
   return do_combine(cfg, T, y, inv, wts, out, s, tr);
 }
 

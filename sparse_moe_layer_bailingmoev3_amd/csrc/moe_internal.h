@@ -33,17 +33,24 @@ struct RouterPlan {
 };
 RouterPlan router_plan(int64_t T, int H, int E);
 size_t router_partial_bytes(int64_t T, int H, int E);
+// `clear` (optional): words zeroed by the logits kernel (the fused forward's dispatch bitmap
+// and counters, which the top-k kernel then fills)
 hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const float* w, int T, int H,
-                                int E, float* partial, hipStream_t s, Tracer* tr = nullptr);
+                                int E, float* partial, uint32_t* clear, int64_t clear_words, hipStream_t s,
+                                Tracer* tr = nullptr);
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G,
                               int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
-                              hipStream_t s, Tracer* tr = nullptr);
+                              uint32_t* bitmap, int32_t* counts, hipStream_t s, Tracer* tr = nullptr);
 
 // ---- dispatch ----------------------------------------------------------------
 size_t dispatch_bitmap_words(int64_t T, int E);
+// marked: the bitmap and counts were already filled by the router's top-k kernel (and
+// cleared by its logits kernel).  tile_prefix (optional): tiles of bm positions per expert.
+// counts: the histogram (cleared and filled here unless marked); counts_out receives a copy
+// plus the shared expert's entry (may equal counts)
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, uint32_t* bitmap,
-                           int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
-                           hipStream_t s, Tracer* tr = nullptr);
+                           int32_t* counts, int32_t* counts_out, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                           bool marked, int32_t* tile_prefix, int bm, hipStream_t s, Tracer* tr = nullptr);
 
 // ---- expert FFN --------------------------------------------------------------
 struct FfnWeights {
@@ -55,13 +62,15 @@ struct FfnWeights {
 struct FfnPlan {
   int mf;      // 16-token fragments per tile
   int bm;      // tokens per tile = 16 * mf
+  int rbw_gate_up, rbw_down;  // 128-row weight blocks per workgroup
   int64_t max_tiles;
 };
 FfnPlan ffn_plan(int64_t T, int K, int E, int S);
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
                              const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
-                             uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr = nullptr);
+                             uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
+                             Tracer* tr = nullptr);
 
 // ---- combine -----------------------------------------------------------------
 hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,

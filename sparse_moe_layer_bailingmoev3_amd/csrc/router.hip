@@ -44,8 +44,17 @@ __device__ __forceinline__ void split3(float w0, float w1, uint32_t& hi, uint32_
 template <int MF, int RF>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w, int T, int H,
-                                                            int E, int kchunk, float* __restrict__ partial) {
+                                                            int E, int kchunk, float* __restrict__ partial,
+                                                            uint32_t* __restrict__ clear, int64_t clear_words) {
   constexpr int WG_EXPERTS = 4 * RF * 16;
+  // zero the dispatch bitmap and counters that the top-k kernel fills (used by the fused
+  // forward; independent of the logits)
+  if (clear) {
+    const int64_t nth = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < clear_words;
+         i += nth)
+      clear[i] = 0u;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int n_tiles = E / WG_EXPERTS;
@@ -123,7 +132,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int T, int E, const float* __restrict__ bias, int G,
                                                           int TG, int K, int norm, float scale,
                                                           int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w) {
+                                                          float* __restrict__ topk_w,
+                                                          uint32_t* __restrict__ bitmap, int words,
+                                                          int32_t* __restrict__ counts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -133,6 +144,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   float l[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) l[i] = 0.f;
+#pragma unroll 4
   for (int p = 0; p < nsplit; ++p) {
     const float* src = partial + ((size_t)p * T + t) * E + e0;
 #pragma unroll
@@ -204,6 +216,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     const float wv = norm ? (my_s / sum) * scale : my_s * scale;
     topk_idx[(size_t)t * K + pos] = my_idx;
     topk_w[(size_t)t * K + pos] = wv;
+    if (bitmap) {
+      // dispatch: one bit per (expert, token) and the expert histogram (integer atomics,
+      // so the final values do not depend on their order)
+      atomicOr(&bitmap[(size_t)my_idx * words + (t >> 5)], 1u << (t & 31));
+      atomicAdd(&counts[my_idx], 1);
+    }
   }
 }
 
@@ -215,15 +233,17 @@ RouterPlan router_plan(int64_t T, int H, int E) {
   RouterPlan p;
   p.mf = pick_router_mf(T);
   p.m_tiles = (int)((T + 16 * p.mf - 1) / (16 * p.mf));
-  p.rf = (E % 128 == 0) ? 2 : 1;
+  // large T: 128 experts per workgroup (x re-read E/128 times); small T: 64 for more blocks
+  p.rf = (E % 128 == 0 && p.m_tiles >= 32) ? 2 : 1;
   p.n_tiles = E / (64 * p.rf);
-  // split the hidden dimension until ~256 workgroups exist (the chip has 256 CUs); each
-  // split is a multiple of 32 that divides H
+  // split the hidden dimension while there are fewer than ~256 workgroups (the chip has
+  // 256 CUs); each split is a multiple of 32 that divides H, and at most 10 splits keep
+  // the partial sums the top-k kernel adds small
   const int kb = H / 32;
   int best = 1;
-  for (int ns = 1; ns <= kb; ++ns) {
+  for (int ns = 1; ns <= std::min(kb, 10); ++ns) {
     if (kb % ns) continue;
-    if ((int64_t)p.m_tiles * p.n_tiles * ns > 320) break;
+    if ((int64_t)p.m_tiles * p.n_tiles * best >= 256) break;
     best = ns;
   }
   p.nsplit = best;
@@ -236,10 +256,12 @@ size_t router_partial_bytes(int64_t T, int H, int E) {
 }
 
 hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const float* w, int T, int H, int E,
-                                float* partial, hipStream_t s, Tracer* tr) {
+                                float* partial, uint32_t* clear, int64_t clear_words, hipStream_t s, Tracer* tr) {
   dim3 grid(p.n_tiles * p.nsplit, p.m_tiles), block(256);
   const int kchunk = H / p.nsplit;
-#define MOE_RL(M, R) hipLaunchKernelGGL((router_logits_kernel<M, R>), grid, block, 0, s, x, w, T, H, E, kchunk, partial)
+#define MOE_RL(M, R)                                                                                         \
+  hipLaunchKernelGGL((router_logits_kernel<M, R>), grid, block, 0, s, x, w, T, H, E, kchunk, partial, clear, \
+                     clear_words)
   if (p.rf == 2) {
     switch (p.mf) {
       case 1: MOE_RL(1, 2); break;
@@ -262,13 +284,14 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
 }
 
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G, int TG,
-                              int K, int norm, float scale, int32_t* topk_idx, float* topk_w, hipStream_t s,
-                              Tracer* tr) {
+                              int K, int norm, float scale, int32_t* topk_idx, float* topk_w, uint32_t* bitmap,
+                              int32_t* counts, hipStream_t s, Tracer* tr) {
+  const int words = (T + 31) / 32;
   dim3 grid((T + 3) / 4), block(256);
   const int epl = E / WAVE;
 #define MOE_TOPK(N)                                                                                          \
   hipLaunchKernelGGL(router_topk_kernel<N>, grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, norm, \
-                     scale, topk_idx, topk_w)
+                     scale, topk_idx, topk_w, bitmap, words, counts)
   switch (epl) {
     case 1: MOE_TOPK(1); break;
     case 2: MOE_TOPK(2); break;
