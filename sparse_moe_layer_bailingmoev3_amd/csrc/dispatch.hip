@@ -46,9 +46,12 @@ __device__ __forceinline__ int wave_sum_prefix(const int32_t* __restrict__ v, in
   return c;
 }
 
-// Waves 0..E-1: expert e.  Wave E: offsets, counts_out (a copy of the histogram plus the
-// shared expert's T*S), the shared expert's identity block and (if tile_prefix) the tile
-// prefix of the E + S experts for tiles of bm positions.
+// Waves 0 .. E*nchunks-1: expert e = wave / nchunks, chunk c = wave % nchunks of 64 bitmap
+// words (2048 tokens) of its row; the chunk's first position is the sum of the counts of
+// the experts before e plus the bits of the row's earlier chunks.  Wave E*nchunks: offsets,
+// counts_out (a copy of the histogram plus the shared expert's T*S), the shared expert's
+// identity block and (if tile_prefix) the tile prefix of the E + S experts for tiles of bm
+// positions.
 __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __restrict__ bitmap,
                                                               const int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ counts_out,
@@ -59,9 +62,10 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
                                                               int32_t* __restrict__ inv_perm,
                                                               int32_t* __restrict__ tile_prefix, int bm) {
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e > E) return;
-  if (e == E) {
+  const int nchunks = (words + WAVE - 1) / WAVE;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv > E * nchunks) return;
+  if (wv == E * nchunks) {
     // exclusive scan of counts[0..E) plus the shared expert
     const int per = (E + WAVE - 1) / WAVE;
     const int b = lane * per, en = min(E, b + per);
@@ -104,35 +108,45 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
       for (int t = lane; t < T; t += WAVE) sorted_token[routed + t] = t;
     return;
   }
-  int base = wave_sum_prefix(counts, e, lane);
-  const int end = base + counts[e];
+  const int e = wv / nchunks, chunk = wv - e * nchunks;
   const uint32_t* row = bitmap + (size_t)e * words;
-  for (int w0 = 0; w0 < words; w0 += WAVE) {
-    const int w = w0 + lane;
-    uint32_t bits = w < words ? row[w] : 0u;
-    const int c = __popc(bits);
-    int incl = c;
+  const int w0 = chunk * WAVE;
+  // start of this chunk: experts before e, then the row's earlier words
+  int base = wave_sum_prefix(counts, e, lane);
+  {
+    int c = 0;
+    for (int w = lane; w < w0; w += WAVE) c += __popc(row[w]);
 #pragma unroll
-    for (int m = 1; m < WAVE; m <<= 1) {
-      int o = __shfl_up(incl, m, WAVE);
-      if (lane >= m) incl += o;
-    }
-    int pos = base + incl - c;
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int t = w * 32 + bit;
-      sorted_token[pos] = t;
-      const int32_t* ti = topk_idx + (size_t)t * K;
-      for (int k = 0; k < K; ++k)
-        if (ti[k] == e) inv_perm[(size_t)t * K + k] = pos;
-      ++pos;
-    }
-    base += __shfl(incl, WAVE - 1, WAVE);
+    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, WAVE);
+    base += c;
   }
-  // a token listing the same expert twice is counted twice but has one bit: mark the
-  // positions that no token fills (the expert FFN skips negative tokens)
-  for (int p = base + lane; p < end; p += WAVE) sorted_token[p] = -1;
+  const int w = w0 + lane;
+  uint32_t bits = w < words ? row[w] : 0u;
+  const int c = __popc(bits);
+  int incl = c;
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) {
+    int o = __shfl_up(incl, m, WAVE);
+    if (lane >= m) incl += o;
+  }
+  int pos = base + incl - c;
+  while (bits) {
+    const int bit = __ffs(bits) - 1;
+    bits &= bits - 1;
+    const int t = w * 32 + bit;
+    sorted_token[pos] = t;
+    const int32_t* ti = topk_idx + (size_t)t * K;
+    for (int k = 0; k < K; ++k)
+      if (ti[k] == e) inv_perm[(size_t)t * K + k] = pos;
+    ++pos;
+  }
+  if (chunk == nchunks - 1) {
+    // a token listing the same expert twice is counted twice but has one bit: mark the
+    // positions that no token fills (the expert FFN skips negative tokens)
+    const int filled = base + __shfl(incl, WAVE - 1, WAVE);
+    const int end = wave_sum_prefix(counts, e, lane) + counts[e];
+    for (int p = filled + lane; p < end; p += WAVE) sorted_token[p] = -1;
+  }
 }
 
 }  // namespace
@@ -155,7 +169,8 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, 
                        E, words, bitmap, counts, inv_perm);
     if (tr) tr->mark("dispatch_mark", s);
   }
-  const int eb = (E + 1 + 3) / 4;
+  const int nchunks = (words + WAVE - 1) / WAVE;
+  const int eb = (E * nchunks + 1 + 3) / 4;
   hipLaunchKernelGGL(dispatch_finish_kernel, dim3(eb), dim3(256), 0, s, bitmap, counts, counts_out, topk_idx, T, K, E,
                      words, S, offsets, sorted_token, inv_perm, tile_prefix, bm);
   if (tr) tr->mark("dispatch_finish", s);

@@ -21,7 +21,7 @@
 //     and the down projection runs one MFMA per plane, so h keeps ~16 significand bits
 //     through the down GEMM; the down projection writes fp32 expert outputs;
 //   * MXFP4 weights (KS = 128: one 16-byte load = 32 codes = one scale block per lane) are
-//     decoded exactly to bf16 in registers;
+//     decoded exactly to bf16 in registers by the gfx950 scaled fp4 -> bf16 conversion;
 //   * the work list (tiles per expert) lives on the device; consecutive work ids are placed
 //     on the same XCD so the row blocks of one tile share its token rows in that XCD's L2.
 #include "moe_common.h"
@@ -53,29 +53,20 @@ struct FfnArgs {
   int nrb;                      // row blocks per expert (N / rows per workgroup)
   int rbw;                      // row blocks one workgroup streams back to back
   int ngroups;                  // ceil(nrb / rbw): row-block groups per tile
+  int bm_list;                  // positions per tile of the device tile list (a multiple of 16*MF)
   float limit, shared_limit;
 };
 
 __device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// e2m1 code (sign<<3 | magnitude code) times a power of two, as an fp32 bit pattern.
-// Magnitudes: code 0 -> 0, 1 -> 0.5, c >= 2 -> (1 + (c&1)/2) * 2^((c>>1) - 1).
-__device__ __forceinline__ uint32_t e2m1_scaled_bits(uint32_t nib, float scale) {
-  const uint32_t c = nib & 7u;
-  uint32_t mag = (c < 2u) ? (c ? 0x3F000000u : 0u) : ((((c >> 1) + 126u) << 23) | ((c & 1u) << 22));
-  float v = __uint_as_float(mag) * scale;  // exact: at most two significant bits
-  return __float_as_uint(v) | ((nib & 8u) << 28);
-}
-
-// 8 codes (low nibble first) -> 8 bf16 (exact, so truncation is the conversion)
+// 8 e2m1 codes (low nibble first) times a power of two -> 8 bf16 (exact).  gfx950 converts
+// one byte (two codes, low nibble to the low half) per instruction.
 __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t v, float scale) {
   u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t b0 = e2m1_scaled_bits((v >> (8 * i)) & 0xFu, scale);
-    uint32_t b1 = e2m1_scaled_bits((v >> (8 * i + 4)) & 0xFu, scale);
-    o[i] = (b0 >> 16) | (b1 & 0xFFFF0000u);
-  }
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3));
   return o;
 }
 
@@ -216,26 +207,28 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
       const int col = FP4 ? q * 32 + s * 8 : s * 32 + q * 8;
-      u32x4 tf[NTP][MF];
-#pragma unroll
-      for (int p = 0; p < NTP; ++p)
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) tf[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
+      u32x4 wf[NMAT][RF];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-          u32x4 wf;
           if constexpr (FP4) {
-            wf = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+            wf[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
           } else {
-            wf = st.w[m][f][s];
+            wf[m][f] = st.w[m][f][s];
           }
-#pragma unroll
-          for (int p = NTP - 1; p >= 0; --p)
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = mfma16(wf, tf[p][mf], acc[m][f][mf]);
         }
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+#pragma unroll
+        for (int p = NTP - 1; p >= 0; --p) {
+          const u32x4 tf = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[m][f], tf, acc[m][f][mf]);
+        }
+      }
     }
   };
 
@@ -313,14 +306,18 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
   __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 16)];
 
-  // device work list: work id -> (tile, row block); tiles of one XCD are consecutive
-  const int total = a.tile_prefix[a.E + a.S] * a.ngroups;
+  // device work list: work id -> (tile, sub-tile, row-block group); consecutive work ids
+  // run on the same XCD.  A tile of the list holds bm_list positions and splits into
+  // bm_list / BM sub-tiles of this kernel's size (empty sub-tiles exit at once).
+  const int subs = a.bm_list / BM;
+  const int total = a.tile_prefix[a.E + a.S] * subs * a.ngroups;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
   if (slot >= per_xcd) return;
   const int w = (blockIdx.x & 7) * per_xcd + slot;
   if (w >= total) return;
-  const int tile = w / a.ngroups, grp = w - tile * a.ngroups;
+  const int tsub = w / a.ngroups, grp = w - tsub * a.ngroups;
+  const int tile = tsub / subs, sub = tsub - tile * subs;
   const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
   int lo = 0, hi = a.E + a.S;
   while (hi - lo > 1) {
@@ -328,8 +325,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
     if (a.tile_prefix[mid] <= tile) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int m0 = (tile - a.tile_prefix[e]) * BM;
+  const int m0 = (tile - a.tile_prefix[e]) * a.bm_list + sub * BM;
   const int cnt = a.offsets[e + 1] - a.offsets[e];
+  if (m0 >= cnt) return;
   const int nrows = min(BM, cnt - m0);
   if constexpr (FMT == FMT_MXFP4) {
     if (e < a.E) {
@@ -362,19 +360,28 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
   }
 }
 
-// rows of weights per workgroup (NW * RF * 16) is 128 in every configuration
+// Kernel configuration per (tile size, weight format, GEMM): NW waves, RF 16-row weight
+// blocks per wave (rows per workgroup NW*RF*16 = 128), D steps of loads in flight.  The down
+// GEMM reads two h planes per token fragment, so it keeps two weight blocks per wave to halve
+// its LDS reads per MFMA.
+template <int MF, int FMT, int MODE> struct FfnCfg {
+  static constexpr bool FP4 = FMT == FMT_MXFP4;
+  static constexpr bool DOWN = MODE == MODE_DOWN;
+  static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
+  static constexpr int RF = (MF <= 2 || DOWN) ? 2 : 1;
+  static constexpr int D = MF <= 2 ? (FP4 ? 3 : 4)
+                         : MF == 4 ? (FP4 ? 2 : 4)
+                         : MF == 8 ? (FP4 ? 2 : (DOWN ? 3 : 4))
+                                   : 2;
+};
 constexpr int FFN_ROWS = 128;
-template <int MF, int FMT> struct FfnCfg;
-template <int FMT> struct FfnCfg<1, FMT> { static constexpr int NW = 4, RF = 2, D = FMT == FMT_MXFP4 ? 3 : 4; };
-template <int FMT> struct FfnCfg<2, FMT> { static constexpr int NW = 4, RF = 2, D = FMT == FMT_MXFP4 ? 3 : 4; };
-template <int FMT> struct FfnCfg<4, FMT> { static constexpr int NW = 8, RF = 1, D = FMT == FMT_MXFP4 ? 2 : 4; };
-template <int FMT> struct FfnCfg<8, FMT> { static constexpr int NW = 8, RF = 1, D = FMT == FMT_MXFP4 ? 2 : 4; };
 
 template <int MF, int MODE, int FMT>
 hipError_t launch_one(const FfnArgs& a, int64_t max_tiles, hipStream_t s, Tracer* tr) {
-  using C = FfnCfg<MF, FMT>;
+  using C = FfnCfg<MF, FMT, MODE>;
   static_assert(C::NW * C::RF * 16 == FFN_ROWS, "rows per workgroup");
-  int64_t work = max_tiles * a.ngroups;
+  if (a.bm_list % (16 * MF)) return hipErrorInvalidValue;
+  int64_t work = max_tiles * (a.bm_list / (16 * MF)) * a.ngroups;
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT>), dim3((unsigned)grid), dim3(C::NW * 64), 0, s, a);
@@ -383,25 +390,37 @@ hipError_t launch_one(const FfnArgs& a, int64_t max_tiles, hipStream_t s, Tracer
   return err;
 }
 
-template <int MF>
-hipError_t launch_mf(const FfnArgs& gu, const FfnArgs& dn, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr) {
-  hipError_t err;
+template <int MODE>
+hipError_t launch_mode(int mf, const FfnArgs& a, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr) {
   if (fmt == FMT_MXFP4) {
-    err = launch_one<MF, MODE_GATEUP, FMT_MXFP4>(gu, max_tiles, s, tr);
-    if (err != hipSuccess) return err;
-    return launch_one<MF, MODE_DOWN, FMT_MXFP4>(dn, max_tiles, s, tr);
+    switch (mf) {
+      case 1: return launch_one<1, MODE, FMT_MXFP4>(a, max_tiles, s, tr);
+      case 2: return launch_one<2, MODE, FMT_MXFP4>(a, max_tiles, s, tr);
+      case 4: return launch_one<4, MODE, FMT_MXFP4>(a, max_tiles, s, tr);
+      case 8: return launch_one<8, MODE, FMT_MXFP4>(a, max_tiles, s, tr);
+      default: return hipErrorInvalidValue;  // the plan never picks 16 for MXFP4
+    }
   }
-  err = launch_one<MF, MODE_GATEUP, FMT_BF16>(gu, max_tiles, s, tr);
-  if (err != hipSuccess) return err;
-  return launch_one<MF, MODE_DOWN, FMT_BF16>(dn, max_tiles, s, tr);
+  switch (mf) {
+    case 1: return launch_one<1, MODE, FMT_BF16>(a, max_tiles, s, tr);
+    case 2: return launch_one<2, MODE, FMT_BF16>(a, max_tiles, s, tr);
+    case 4: return launch_one<4, MODE, FMT_BF16>(a, max_tiles, s, tr);
+    case 8: return launch_one<8, MODE, FMT_BF16>(a, max_tiles, s, tr);
+    default: return launch_one<16, MODE, FMT_BF16>(a, max_tiles, s, tr);
+  }
 }
 
 }  // namespace
 
-FfnPlan ffn_plan(int64_t T, int K, int E, int S) {
+FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt) {
   FfnPlan p;
   const double avg = (double)T * K / E;  // routed tokens per expert on average
-  p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : 8;
+  // tile list of 16*mf positions; gate/up runs whole tiles, down runs sub-tiles of 16*mf_down
+  // (measured: the down GEMM, which reads two h planes, is fastest with 64-token tiles at
+  // two waves per SIMD; gate/up with 128, or 256 when experts average well above 128 tokens)
+  p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : (avg <= 192 || fmt == FMT_MXFP4) ? 8 : 16;
+  p.mf_gate_up = p.mf;
+  p.mf_down = std::min(p.mf, 4);
   p.bm = 16 * p.mf;
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
@@ -441,12 +460,10 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   dn.rbw = std::min(dn.nrb, p.rbw_down);
   dn.ngroups = (dn.nrb + dn.rbw - 1) / dn.rbw;
 
-  switch (p.mf) {
-    case 1: return launch_mf<1>(gu, dn, w.fmt, p.max_tiles, s, tr);
-    case 2: return launch_mf<2>(gu, dn, w.fmt, p.max_tiles, s, tr);
-    case 4: return launch_mf<4>(gu, dn, w.fmt, p.max_tiles, s, tr);
-    default: return launch_mf<8>(gu, dn, w.fmt, p.max_tiles, s, tr);
-  }
+  gu.bm_list = dn.bm_list = p.bm;
+  err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, w.fmt, p.max_tiles, s, tr);
+  if (err != hipSuccess) return err;
+  return launch_mode<MODE_DOWN>(p.mf_down, dn, w.fmt, p.max_tiles, s, tr);
 }
 
 }  // namespace moe

@@ -60,12 +60,13 @@ struct FfnWeights {
   int fmt;
 };
 struct FfnPlan {
-  int mf;      // 16-token fragments per tile
+  int mf;      // 16-token fragments per tile of the tile list (1, 2, 4, 8; 16 for bf16 weights)
+  int mf_gate_up, mf_down;  // fragments per workgroup of each GEMM (divide mf)
   int bm;      // tokens per tile = 16 * mf
   int rbw_gate_up, rbw_down;  // 128-row weight blocks per workgroup
   int64_t max_tiles;
 };
-FfnPlan ffn_plan(int64_t T, int K, int E, int S);
+FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt);
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
                              const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
