@@ -412,7 +412,7 @@ hipError_t launch_mode(int mf, const FfnArgs& a, int fmt, int64_t max_tiles, hip
 
 }  // namespace
 
-FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt) {
+FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   FfnPlan p;
   const double avg = (double)T * K / E;  // routed tokens per expert on average
   // tile list of 16*mf positions; gate/up runs whole tiles, down runs sub-tiles of 16*mf_down
@@ -421,6 +421,9 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt) {
   p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : (avg <= 192 || fmt == FMT_MXFP4) ? 8 : 16;
   p.mf_gate_up = p.mf;
   p.mf_down = std::min(p.mf, 4);
+  // many tokens per expert and bf16 weights: the 256-token tile kernel (ffn_tile.hip)
+  p.tiles = fmt == FMT_BF16 && avg > 48 && ffn_tiles_supported(H, I);
+  if (p.tiles) p.mf = 16;
   p.bm = 16 * p.mf;
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
@@ -436,6 +439,16 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
                              bool tiles_ready, hipStream_t s, Tracer* tr) {
   hipError_t err = hipSuccess;
+  if (p.tiles) {
+    if (!tiles_ready) {
+      hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
+      err = hipGetLastError();
+      if (tr) tr->mark("expert_tiles", s);
+      if (err != hipSuccess) return err;
+    }
+    return launch_expert_ffn_tiles(x, offsets, sorted_token, tile_prefix, p.max_tiles, w, T, H, I, E, S, limit,
+                                   shared_limit, h_hi, h_lo, y, s, tr);
+  }
   if (!tiles_ready) {
     hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
     err = hipGetLastError();

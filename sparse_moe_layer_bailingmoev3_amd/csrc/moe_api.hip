@@ -178,7 +178,8 @@ moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, i
                          int32_t* sorted_token, int32_t* inv_perm, const Layout& L, void* ws, hipStream_t s,
                          moe::Tracer* tr = nullptr, bool marked = false, bool with_tiles = false) {
   moe::FfnPlan fp = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
-                                   c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16);
+                                   c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                                   c->hidden_size, c->moe_intermediate_size);
   int32_t* hist = marked ? (int32_t*)at(ws, L.counts) : counts;
   hipError_t e = moe::launch_dispatch(idx, (int)T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
                                       (uint32_t*)at(ws, L.bitmap), hist, counts, offsets, sorted_token, inv_perm,
@@ -191,7 +192,8 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32
                     const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
                     hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false) {
   moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
-                                  c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16);
+                                  c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                                  c->hidden_size, c->moe_intermediate_size);
   const float lim = c->swiglu_limit > 0 ? c->swiglu_limit : 0.f;
   const float slim = c->shared_swiglu_limit > 0 ? c->shared_swiglu_limit : 0.f;
   hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),

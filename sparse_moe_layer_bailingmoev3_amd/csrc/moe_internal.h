@@ -64,14 +64,22 @@ struct FfnPlan {
   int mf_gate_up, mf_down;  // fragments per workgroup of each GEMM (divide mf)
   int bm;      // tokens per tile = 16 * mf
   int rbw_gate_up, rbw_down;  // 128-row weight blocks per workgroup
+  bool tiles;  // use the 256-token tile kernel (bm = 256)
   int64_t max_tiles;
 };
-FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt);
+FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I);
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
                              const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr);
+
+// 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles
+bool ffn_tiles_supported(int H, int I);
+hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
+                                   const int32_t* tile_prefix, int64_t max_tiles, const FfnWeights& w, int T, int H,
+                                   int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
+                                   uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr);
 
 // ---- combine -----------------------------------------------------------------
 hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,
