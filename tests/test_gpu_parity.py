@@ -130,6 +130,43 @@ def test_stages_tiny():
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * rms(ref))
 
 
+@pytest.mark.parametrize("T", [385, 2048, 4099])
+def test_forward_tiny_large_tiles(T):
+    # T*K/E above 48 tokens per expert selects the 256-position tile kernels; at T = 2048 and
+    # 4099 many experts span two or more tiles and the last tile of each is ragged
+    check_forward(host_case(CONFIGS["tiny"], seed=14, T=T))
+
+
+def test_forward_tiles_unsupported_shape():
+    # hidden 384 is not a multiple of the 256-row down block: many tokens per expert must
+    # still be served, by the small-tile kernels
+    check_forward(host_case(CONFIGS["tiny"].with_(hidden_size=384), seed=15, T=1000))
+
+
+@pytest.mark.parametrize("T", [40, 1000])
+def test_forward_tiny_mxfp4(T):
+    s = CONFIGS["tiny"].with_(weight_format="mxfp4")
+    bf = gen_experts(CONFIGS["tiny"], seed=16)
+    ex = {}
+    for k in ("gate", "up", "down"):
+        qs = [quantise_mxfp4(bf[k][e]) for e in range(s.E)]
+        ex[k + "_q"] = np.stack([a for a, _ in qs])
+        ex[k + "_s"] = np.stack([b for _, b in qs])
+    check_forward(host_case(s, seed=16, T=T, experts=ex), tol=TOL_MXFP4)
+
+
+def test_determinism_tiny_tiles():
+    import torch
+    c = host_case(CONFIGS["tiny"], seed=17, T=2048)
+    dev = DeviceCase(c)
+    say("[gpu] moe_forward twice, tiny T=2048 (256-position tiles)")
+    a = [t.clone() for t in dev.forward()]
+    b = dev.forward()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
 def test_determinism_tiny():
     import torch
     c = host_case(CONFIGS["tiny"], seed=8, T=300)
