@@ -380,7 +380,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
-    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ from the rocprofv3 runs in DIR and exit")
     args = ap.parse_args()
