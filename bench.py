@@ -152,34 +152,48 @@ def measure(shape, d, steps, warmup, hip):
         moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
     torch.cuda.synchronize()
 
-    # timed region: `steps` traced forwards; events between kernels cost no GPU work
+    # per-kernel breakdown, outside the timed region: forwards with an event after every kernel
+    # (each recorded event adds a few microseconds of queue time to the step)
     nev = 24
-    events = [[hip.event() for _ in range(nev)] for _ in range(steps)]
+    nb = max(3, min(steps, 10))
+    events = [[hip.event() for _ in range(nev)] for _ in range(nb)]
+    names = None
+    for s in range(nb):
+        names = moe.moe_forward_traced(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, events[s])
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for s in range(nb):
+        for i, n in enumerate(names):
+            per_kernel.setdefault(n, []).append(hip.elapsed_ms(events[s][i], events[s][i + 1]))
+    kmean = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    dom = max(("expert_gate_up", "expert_down"), key=lambda n: kmean.get(n, 0.0))
+    k = names.index(dom)
+
+    # timed region: `steps` forwards, each with the two events around its dominant kernel only
+    timed = [[None] * (len(names) + 1) for _ in range(steps)]
+    for s in range(steps):
+        timed[s][k], timed[s][k + 1] = hip.event(), hip.event()
     t_start, t_end = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(t_start, stream)
-    names = None
     for s in range(steps):
-        names = moe.moe_forward_traced(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, events[s])
+        moe.moe_forward_traced(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, timed[s])
     hip.record(t_end, stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = hip.elapsed_ms(t_start, t_end) / steps
-    per_kernel = {}
-    for s in range(steps):
-        for i, n in enumerate(names):
-            per_kernel.setdefault(n, []).append(hip.elapsed_ms(events[s][i], events[s][i + 1]))
-    kmean = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    dom_ms = float(np.mean([hip.elapsed_ms(timed[s][k], timed[s][k + 1]) for s in range(steps)]))
     # routing of the last step (for algorithmic bytes)
     moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
     torch.cuda.synchronize()
     counts = cnt.cpu().numpy()
-    return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, counts=counts, out=out)
+    return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, dom=dom, dom_ms=dom_ms, counts=counts, out=out)
 
 
 def roofline(shape, r, workload=None):
-    """Roofline of the dominant kernel (the longest of the step).
+    """Roofline of the dominant kernel (the longer of gate/up and down), timed by the two
+    events around it in every step of the timed region.
 
     Algorithmic bytes per launch (what the method has to move, once):
       expert_gate_up: (touched routed experts + shared) * 2*I*H weights in their storage
@@ -194,15 +208,14 @@ def roofline(shape, r, workload=None):
     eb = expert_bytes(shape)
     per_mat = eb // 3
     sh_mat = 2 * H * I  # shared expert is bf16
-    ks = r["kernels"]
-    dom = max(("expert_gate_up", "expert_down"), key=lambda n: ks.get(n, 0.0))
+    dom = r["dom"]
     if dom == "expert_gate_up":
         byts = touched * 2 * per_mat + S * 2 * sh_mat + T * H * 2 + pairs * I * 2
         flops = 4.0 * H * I * pairs
     else:
         byts = touched * per_mat + S * sh_mat + pairs * I * 2 + pairs * H * 4
         flops = 2.0 * H * I * pairs
-    ms = ks[dom]
+    ms = r["dom_ms"]
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     hbm_time = byts / (HBM_PEAK_GBS * 1e9)
@@ -242,123 +255,23 @@ def cpu_baseline(shape, d, experts, max_tokens):
             return tuple(oracle.mxfp4_dequant(experts[k + "_q"][e], experts[k + "_s"][e]) for k in ("gate", "up", "down"))
         return tuple(oracle.bf16_to_f64(experts[k][e]) for k in ("gate", "up", "down"))
     sh = tuple(oracle.bf16_to_f64(d["shared_np"][k]) for k in ("gate", "up", "down"))
-    t0 = time.perf_counter()
-    oracle.moe_layer(x, d["router_w_np"], d["bias_np"], get, sh, n_group=shape.G, topk_group=shape.TG,
-                     top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
-                     norm_topk_prob=shape.norm_topk_prob, swiglu_limit=shape.swiglu_limit,
-                     shared_swiglu_limit=shape.shared_swiglu_limit)
-    dt = time.perf_counter() - t0
+    # the whole sample again until about 10 s of CPU work have been timed
+    passes, dt = 0, 0.0
+    while passes == 0 or (dt < 10.0 and passes < 50):
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, d["router_w_np"], d["bias_np"], get, sh, n_group=shape.G, topk_group=shape.TG,
+                         top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
+                         norm_topk_prob=shape.norm_topk_prob, swiglu_limit=shape.swiglu_limit,
+                         shared_swiglu_limit=shape.shared_swiglu_limit)
+        dt += time.perf_counter() - t0
+        passes += 1
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return dict(value=round(T / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=round(T * passes / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"float64 oracle forward of the first {T} tokens of the {shape.name} workload "
-                       f"(H{shape.H}/E{shape.E}/top{shape.K}), {dt:.1f} s")
-
-
-# ----------------------------------------------------------------------------------
-# rocprofv3 summaries (profiles/*.md) and the traffic record (profiles/traffic.json)
-# ----------------------------------------------------------------------------------
-# kernel symbol in rocprofv3 output -> the step name moe_forward_traced reports
-SYMBOL_STEPS = [(r"^ffn_tile_kernel<0,", "expert_gate_up"), (r"^ffn_tile_kernel<1,", "expert_down"),
-                (r"^ffn_kernel<\d+, \d+, \d+, \d+, 0,", "expert_gate_up"),
-                (r"^ffn_kernel<\d+, \d+, \d+, \d+, 1,", "expert_down"),
-                (r"^router_logits_kernel", "router_logits"), (r"^router_topk_kernel", "router_topk"),
-                (r"^fill_u32_kernel", "dispatch_clear"), (r"^dispatch_mark_kernel", "dispatch_mark"),
-                (r"^dispatch_finish_kernel", "dispatch_finish"), (r"^tile_prefix_kernel", "expert_tiles"),
-                (r"^combine_kernel", "combine"), (r"^__amd_rocclr_copyBuffer", "copy")]
-
-
-def _symbol(name: str) -> str:
-    import re
-    n = name.replace("void ", "").replace("moe::(anonymous namespace)::", "").replace("moe::", "")
-    return re.sub(r"\(.*", "", n)
-
-
-def _step(sym: str):
-    import re
-    for pat, step in SYMBOL_STEPS:
-        if re.match(pat, sym):
-            return step
-    return None
-
-
-def profile_commands(workload: str, out: str = "$OUT"):
-    b = f"python3 $R/bench.py --workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-prefill --copy-probe"
-    return [f"rocprofv3 --kernel-trace --stats -f csv -d {out}/kt -o kt -- {b}",
-            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/fetch -o fetch -- {b}",
-            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/write -o write -- {b}",
-            f"python3 $R/bench.py --summarize {out} --workload {workload}"]
-
-
-def summarize(src: str, workload: str):
-    """Turn the three rocprofv3 runs of profile_commands() into profiles/<kernel>_<workload>.md
-    and the workload's entry in profiles/traffic.json (HBM bytes per launch of each step, with
-    the kernel-source hash they were taken on)."""
-    import csv
-    import glob
-    from synthetic import CONFIGS
-    shape = CONFIGS[workload]
-
-    def one(pattern):
-        f = glob.glob(os.path.join(src, pattern))
-        if not f:
-            raise SystemExit(f"missing {os.path.join(src, pattern)}")
-        return f[0]
-    stats = [(_symbol(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["Percentage"]))
-             for r in csv.DictReader(open(one("kt/*kernel_stats.csv")))]
-
-    def counters(path, cname):
-        per = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == cname:
-                per.setdefault(_symbol(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
-        return per
-    fetch = counters(one("fetch/*counter_collection.csv"), "FETCH_SIZE")
-    write = counters(one("write/*counter_collection.csv"), "WRITE_SIZE")
-    copy_f, copy_w = max(fetch["__amd_rocclr_copyBuffer"]), max(write["__amd_rocclr_copyBuffer"])
-    sf, sw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
-    steps = {}
-    for sym, c, avg, pct in stats:
-        st = _step(sym)
-        if st and st != "copy":
-            steps[st] = dict(symbol=sym, calls=c, avg_us=avg, pct=pct,
-                             fetch_bytes=float(np.mean(fetch.get(sym, [0.0]))) * 1024 * sf,
-                             write_bytes=float(np.mean(write.get(sym, [0.0]))) * 1024 * sw)
-    dom = max(("expert_gate_up", "expert_down"), key=lambda k: steps.get(k, {}).get("avg_us", 0.0))
-    cmds = profile_commands(workload)
-    lines = [f"# {dom} on the {workload} workload (T={shape.T}, H{shape.H}/E{shape.E}/top{shape.K}, "
-             f"{shape.weight_format} experts)", "",
-             "Commands (from /tmp with TMPDIR=/tmp; $R = repository root, $OUT = an output folder):", "", "```",
-             *cmds, "```", "", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
-             "| kernel | step | calls | average us | % of GPU time |", "|---|---|---|---|---|"]
-    for sym, c, avg, pct in stats:
-        lines.append(f"| `{sym}` | {_step(sym) or ''} | {c} | {avg:.1f} | {pct:.1f} |")
-    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-              f"A plain 1 GiB device copy in the same runs reads FETCH_SIZE = {copy_f:.0f} KiB and "
-              f"WRITE_SIZE = {copy_w:.0f} KiB, so bytes = FETCH_SIZE * 1024 * {sf:.3f} and "
-              f"WRITE_SIZE * 1024 * {sw:.3f}.", "",
-              "| step | kernel | read MB | write MB |", "|---|---|---|---|"]
-    for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
-        lines.append(f"| {st} | `{e['symbol']}` | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} |")
-    os.makedirs(PROFILES, exist_ok=True)
-    md = os.path.join(PROFILES, f"{dom}_{workload}_T{shape.T}.md")
-    with open(md, "w") as fh:
-        fh.write("\n".join(lines) + "\n")
-    try:
-        with open(TRAFFIC_RECORD) as fh:
-            rec = json.load(fh)
-    except (OSError, ValueError):
-        rec = {}
-    h = kernel_source_hash()
-    rec[workload] = {st: dict(symbol=e["symbol"], fetch_bytes=round(e["fetch_bytes"]),
-                              write_bytes=round(e["write_bytes"]), avg_us=round(e["avg_us"], 2), source_sha256=h)
-                     for st, e in steps.items()}
-    with open(TRAFFIC_RECORD, "w") as fh:
-        json.dump(rec, fh, indent=1, sort_keys=True)
-        fh.write("\n")
-    print(open(md).read())
+                       f"(H{shape.H}/E{shape.E}/top{shape.K}), {passes} passes, {dt:.1f} s")
 
 
 def copy_probe(hip, nbytes=1 << 30):
@@ -380,7 +293,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
-    ap.add_argument("--cpu-tokens", type=int, default=512, help="tokens in the CPU oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ from the rocprofv3 runs in DIR and exit")
     args = ap.parse_args()
@@ -434,6 +347,7 @@ def main():
         "roofline": roofline(shape, r),
         "layer": layer_summary(shape, r),
         "kernels_ms": {k: round(v, 4) for k, v in r["kernels"].items()},
+        "kernels_ms_from": "forwards with an event after every kernel, outside the timed region",
         "event_ms_per_step": round(r["event_ms"], 4),
     }
     if not args.no_prefill and shape.name == "decode":

@@ -160,7 +160,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
 
 /* moe_forward with a timing trace, for profiling (same results).  events[0] is recorded on
  * `stream` before the first kernel and events[i+1] right after the i-th kernel launch; the
- * caller creates the events (hipEvent_t, passed as void*) and later reads the elapsed times.
+ * caller creates the events (hipEvent_t, passed as void*) and later reads the elapsed times;
+ * a NULL entry records nothing (each recorded event costs a few microseconds of queue time,
+ * so a caller timing one kernel passes only the two events around it).
  * kernel_names (host array of max_events - 1 pointers) receives static kernel names and
  * *n_kernels the number of kernels launched.  Returns MOE_ERR_INVALID_ARG (after running
  * the layer) if max_events is smaller than n_kernels + 1. */

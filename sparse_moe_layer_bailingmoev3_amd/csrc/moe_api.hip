@@ -332,7 +332,7 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
   int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);
   void* y = at(ws, L.y);
-  if (tr && tr->events && tr->cap > 0) hipEventRecord(tr->events[0], s);
+  if (tr && tr->events && tr->cap > 0 && tr->events[0]) (void)hipEventRecord(tr->events[0], s);
   if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true)) != MOE_OK) return st;
   if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
     return st;

@@ -8,8 +8,9 @@ namespace moe {
 
 enum { FMT_BF16 = 0, FMT_MXFP4 = 1 };
 
-// Optional per-kernel event trace: events[0] is recorded by the caller before the first
-// launch, events[i+1] right after the i-th kernel; names[i] names that kernel.
+// Optional per-kernel event trace: events[0] is recorded before the first launch,
+// events[i+1] right after the i-th kernel (a NULL slot records nothing); names[i] names that
+// kernel.
 struct Tracer {
   hipEvent_t* events = nullptr;
   const char** names = nullptr;
@@ -17,7 +18,7 @@ struct Tracer {
   int n = 0;    // kernels launched so far
   void mark(const char* name, hipStream_t s) {
     if (events && n + 1 < cap) {
-      hipEventRecord(events[n + 1], s);
+      if (events[n + 1]) (void)hipEventRecord(events[n + 1], s);
       names[n] = name;
     }
     ++n;
