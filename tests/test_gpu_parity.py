@@ -167,6 +167,24 @@ def test_determinism_tiny_tiles():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
+# other expert counts, group layouts and fan-outs: one case per top-k kernel instantiation
+# (experts per lane 1, 2, 4, 8, 16) and the degenerate group settings
+LAYOUTS = [
+    dict(num_experts=128, n_group=8, topk_group=4, num_experts_per_tok=8),     # 2 experts per lane
+    dict(num_experts=256, n_group=4, topk_group=2, num_experts_per_tok=6),     # 4 per lane
+    dict(num_experts=1024, n_group=16, topk_group=8, num_experts_per_tok=16),  # 16 per lane, K at its maximum
+    dict(num_experts=64, n_group=1, topk_group=1, num_experts_per_tok=1),      # one group, top-1
+    dict(num_experts=64, n_group=64, topk_group=8, num_experts_per_tok=8),     # one expert per group
+]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda d: "E{num_experts}_G{n_group}_TG{topk_group}_K{num_experts_per_tok}".format(**d))
+@pytest.mark.parametrize("T", [70, 1100])
+def test_forward_layouts(layout, T):
+    s = CONFIGS["tiny"].with_(hidden_size=256, **layout)
+    check_forward(host_case(s, seed=18, T=T))
+
+
 def test_determinism_tiny():
     import torch
     c = host_case(CONFIGS["tiny"], seed=8, T=300)
