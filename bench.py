@@ -274,6 +274,110 @@ def cpu_baseline(shape, d, experts, max_tokens):
                        f"(H{shape.H}/E{shape.E}/top{shape.K}), {passes} passes, {dt:.1f} s")
 
 
+# ----------------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/*.md) and the traffic record (profiles/traffic.json)
+# ----------------------------------------------------------------------------------
+# kernel symbol in rocprofv3 output -> the step name moe_forward_traced reports
+SYMBOL_STEPS = [(r"^ffn_tile_kernel<0,", "expert_gate_up"), (r"^ffn_tile_kernel<1,", "expert_down"),
+                (r"^ffn_kernel<\d+, \d+, \d+, \d+, 0,", "expert_gate_up"),
+                (r"^ffn_kernel<\d+, \d+, \d+, \d+, 1,", "expert_down"),
+                (r"^router_logits_kernel", "router_logits"), (r"^router_topk_kernel", "router_topk"),
+                (r"^fill_u32_kernel", "dispatch_clear"), (r"^dispatch_mark_kernel", "dispatch_mark"),
+                (r"^dispatch_finish_kernel", "dispatch_finish"), (r"^tile_prefix_kernel", "expert_tiles"),
+                (r"^combine_kernel", "combine"), (r"^__amd_rocclr_copyBuffer", "copy")]
+
+
+def _symbol(name: str) -> str:
+    import re
+    n = name.replace("void ", "").replace("moe::(anonymous namespace)::", "").replace("moe::", "")
+    return re.sub(r"\(.*", "", n)
+
+
+def _step(sym: str):
+    import re
+    for pat, step in SYMBOL_STEPS:
+        if re.match(pat, sym):
+            return step
+    return None
+
+
+def profile_commands(workload: str, out: str = "$OUT"):
+    b = f"python3 $R/bench.py --workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-prefill --copy-probe"
+    return [f"rocprofv3 --kernel-trace --stats -f csv -d {out}/kt -o kt -- {b}",
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/fetch -o fetch -- {b}",
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/write -o write -- {b}",
+            f"python3 $R/bench.py --summarize {out} --workload {workload}"]
+
+
+def summarize(src: str, workload: str):
+    """Turn the three rocprofv3 runs of profile_commands() into profiles/<kernel>_<workload>.md
+    and the workload's entry in profiles/traffic.json (HBM bytes per launch of each step, with
+    the kernel-source hash they were taken on)."""
+    import csv
+    import glob
+    from synthetic import CONFIGS
+    shape = CONFIGS[workload]
+
+    def one(pattern):
+        f = glob.glob(os.path.join(src, pattern))
+        if not f:
+            raise SystemExit(f"missing {os.path.join(src, pattern)}")
+        return f[0]
+    stats = [(_symbol(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["Percentage"]))
+             for r in csv.DictReader(open(one("kt/*kernel_stats.csv")))]
+
+    def counters(path, cname):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == cname:
+                per.setdefault(_symbol(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return per
+    fetch = counters(one("fetch/*counter_collection.csv"), "FETCH_SIZE")
+    write = counters(one("write/*counter_collection.csv"), "WRITE_SIZE")
+    copy_f, copy_w = max(fetch["__amd_rocclr_copyBuffer"]), max(write["__amd_rocclr_copyBuffer"])
+    sf, sw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
+    steps = {}
+    for sym, c, avg, pct in stats:
+        st = _step(sym)
+        if st and st != "copy":
+            steps[st] = dict(symbol=sym, calls=c, avg_us=avg, pct=pct,
+                             fetch_bytes=float(np.mean(fetch.get(sym, [0.0]))) * 1024 * sf,
+                             write_bytes=float(np.mean(write.get(sym, [0.0]))) * 1024 * sw)
+    dom = max(("expert_gate_up", "expert_down"), key=lambda k: steps.get(k, {}).get("avg_us", 0.0))
+    cmds = profile_commands(workload)
+    lines = [f"# {dom} on the {workload} workload (T={shape.T}, H{shape.H}/E{shape.E}/top{shape.K}, "
+             f"{shape.weight_format} experts)", "",
+             "Commands (from /tmp with TMPDIR=/tmp; $R = repository root, $OUT = an output folder):", "", "```",
+             *cmds, "```", "", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | step | calls | average us | % of GPU time |", "|---|---|---|---|---|"]
+    for sym, c, avg, pct in stats:
+        lines.append(f"| `{sym}` | {_step(sym) or ''} | {c} | {avg:.1f} | {pct:.1f} |")
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"A plain 1 GiB device copy in the same runs reads FETCH_SIZE = {copy_f:.0f} KiB and "
+              f"WRITE_SIZE = {copy_w:.0f} KiB, so bytes = FETCH_SIZE * 1024 * {sf:.3f} and "
+              f"WRITE_SIZE * 1024 * {sw:.3f}.", "",
+              "| step | kernel | read MB | write MB |", "|---|---|---|---|"]
+    for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
+        lines.append(f"| {st} | `{e['symbol']}` | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    md = os.path.join(PROFILES, f"{dom}_{workload}_T{shape.T}.md")
+    with open(md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    h = kernel_source_hash()
+    rec[workload] = {st: dict(symbol=e["symbol"], fetch_bytes=round(e["fetch_bytes"]),
+                              write_bytes=round(e["write_bytes"]), avg_us=round(e["avg_us"], 2), source_sha256=h)
+                     for st, e in steps.items()}
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(open(md).read())
+
+
 def copy_probe(hip, nbytes=1 << 30):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
     import torch
