@@ -101,6 +101,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
   constexpr int ROWS = NW * RF * 16;
   constexpr int WREGS = FP4 ? 1 : SUB;
+  // loop form (each measured fastest for its kernels): tiles of 64+ tokens and the MXFP4
+  // kernel (128-value steps) issue every load unconditionally; 16- and 32-token tiles do not
+  constexpr bool PADDED = KS == 128 || MF >= 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -110,28 +113,29 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   const bool shared = e == a.E;
   const int pos0 = a.offsets[e] + m0;
 
-  // token tile: per-thread 16-byte pieces (row, col) and their sources (null -> zeros)
+  // token tile: per-thread 16-byte pieces (row, col).  Every piece is loaded from a valid
+  // address (pieces past the tile or of a position without a token read the tile's first
+  // position, or token 0) and the invalid ones are written to LDS as zeros, so every step
+  // issues the same loads and the compiler's wait counting stays exact.
   const uint16_t* tsrc[NTP][CPT];
+  bool tvalid[CPT];
   int tdst[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * NTH;
-#pragma unroll
-    for (int p = 0; p < NTP; ++p) tsrc[p][i] = nullptr;
-    tdst[i] = -1;
-    if (c < CHUNKS) {
-      const int row = c / (KS / 8), col = (c % (KS / 8)) * 8;
-      tdst[i] = row * LROW + col;
-      if (row < nrows) {
-        if (MODE == MODE_GATEUP) {
-          const int tok = a.sorted_token[pos0 + row];
-          if ((unsigned)tok < (unsigned)a.T) tsrc[0][i] = a.act + (size_t)tok * K + col;
-        } else {
-          tsrc[0][i] = a.act + (size_t)(pos0 + row) * K + col;
-          tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + row) * K + col;
-        }
-      }
+    const int row = c < CHUNKS ? c / (KS / 8) : 0, col = (c % (KS / 8)) * 8;
+    tdst[i] = c < CHUNKS ? row * LROW + col : -1;
+    bool ok = c < CHUNKS && row < nrows;
+    const int prow = row < nrows ? row : 0;
+    if (MODE == MODE_GATEUP) {
+      const int tok = a.sorted_token[pos0 + prow];
+      ok = ok && (unsigned)tok < (unsigned)a.T;
+      tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + col;
+    } else {
+      tsrc[0][i] = a.act + (size_t)(pos0 + prow) * K + col;
+      tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + col;
     }
+    tvalid[i] = ok;
   }
 
   // weight rows of this lane.  bf16: sub-step s of a step reads k = 32s + 8q .. +7, so
@@ -170,23 +174,31 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // loads of step `step`; past the last step they repeat the last step's addresses into a
+  // ring slot that is not read again
   auto load_t = [&](TStage<NTP, CPT>& ts, int step) {
-    const int ks = step % nsteps;
+    const int ks = min(step, total_steps - 1) % nsteps;
 #pragma unroll
     for (int p = 0; p < NTP; ++p)
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        ts.t[p][i] = tsrc[p][i] ? *(const u32x4*)(tsrc[p][i] + ks * KS) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < CPT; ++i) {
+        if constexpr (PADDED)
+          ts.t[p][i] = *(const u32x4*)(tsrc[p][i] + ks * KS);
+        else
+          ts.t[p][i] = tvalid[i] ? *(const u32x4*)(tsrc[p][i] + ks * KS) : u32x4{0u, 0u, 0u, 0u};
+      }
   };
   auto store_t = [&](const TStage<NTP, CPT>& ts, int buf) {
 #pragma unroll
     for (int p = 0; p < NTP; ++p)
 #pragma unroll
       for (int i = 0; i < CPT; ++i)
-        if (tdst[i] >= 0) *(u32x4*)(lds + (buf * NTP + p) * BM * LROW + tdst[i]) = ts.t[p][i];
+        if (tdst[i] >= 0)
+          *(u32x4*)(lds + (buf * NTP + p) * BM * LROW + tdst[i]) = tvalid[i] ? ts.t[p][i] : u32x4{0u, 0u, 0u, 0u};
   };
   // (plain loads: nontemporal loads measured ~25% slower on these streams)
   auto load_w = [&](WStage<NMAT, RF, WREGS>& st, int step) {
+    step = min(step, total_steps - 1);
     const int rbi = step / nsteps, ks = step - rbi * nsteps;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -274,26 +286,46 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   TStage<NTP, CPT> ts[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    if (j < total_steps) {
-      load_t(ts[j], j);
-      load_w(ws[j], j);
-    }
+    load_t(ts[j], j);
+    load_w(ws[j], j);
   }
   store_t(ts[0], 0);
   block_sync_lds();
-  for (int s0 = 0; s0 < total_steps; s0 += D) {
+  if constexpr (PADDED) {
+    // the loop runs to a multiple of D steps, every step issuing its loads unconditionally
+    // (the steps past the end repeat the last loads into slots nobody reads), so the
+    // compiler's own wait counting stays exact
+    const int padded_steps = (total_steps + D - 1) / D * D;
+    for (int s0 = 0; s0 < padded_steps; s0 += D) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int s = s0 + j;
-      if (s < total_steps) {
-        if (s + 1 < total_steps) store_t(ts[(j + 1) % D], (s + 1) & 1);
-        compute(ws[j], s & 1);
-        if (s + D < total_steps) {
-          load_t(ts[j], s + D);
-          load_w(ws[j], s + D);
-        }
-        if ((s + 1) % nsteps == 0) epilogue(s / nsteps);
+      for (int j = 0; j < D; ++j) {
+        const int s = s0 + j;
+        const bool real = s < total_steps;
+        if (real && s + 1 < total_steps) store_t(ts[(j + 1) % D], (s + 1) & 1);
+        if (real) compute(ws[j], s & 1);
+        load_t(ts[j], s + D);
+        load_w(ws[j], s + D);
+        if (real && (s + 1) % nsteps == 0) epilogue(s / nsteps);
         block_sync_lds();
+      }
+    }
+  } else {
+    // short blocks of a few tokens (decode): no repeated loads past the end, and only the
+    // positions that hold a token are loaded
+    for (int s0 = 0; s0 < total_steps; s0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int s = s0 + j;
+        if (s < total_steps) {
+          if (s + 1 < total_steps) store_t(ts[(j + 1) % D], (s + 1) & 1);
+          compute(ws[j], s & 1);
+          if (s + D < total_steps) {
+            load_t(ts[j], s + D);
+            load_w(ws[j], s + D);
+          }
+          if ((s + 1) % nsteps == 0) epilogue(s / nsteps);
+          block_sync_lds();
+        }
       }
     }
   }
