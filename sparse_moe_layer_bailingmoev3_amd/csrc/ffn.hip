@@ -460,7 +460,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
   p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
-  p.rbw_down = p.mf >= 4 ? 5 : 4;
+  p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one 128-row block per workgroup (measured)
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
   return p;
