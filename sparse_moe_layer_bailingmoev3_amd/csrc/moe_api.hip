@@ -153,21 +153,26 @@ char* at(void* ws, size_t off) { return (char*)ws + off; }
 
 // mark: also clear (logits kernel) and fill (top-k kernel) the dispatch bitmap and the
 // expert histogram in the workspace, so moe_dispatch's clear and mark kernels are not needed
+// fd (optional, with mark): finish the dispatch inside the top-k kernel; its counter is the
+// histogram's spare last entry
 moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const float* rw, const float* bias,
                       int32_t* idx, float* wts, const Layout& L, void* ws, hipStream_t s,
-                      moe::Tracer* tr = nullptr, bool mark = false) {
+                      moe::Tracer* tr = nullptr, bool mark = false, moe::FusedDispatch* fd = nullptr) {
   moe::RouterPlan p = moe::router_plan(T, c->hidden_size, c->num_experts);
   float* partial = (float*)at(ws, L.partial);
   uint32_t* bitmap = mark ? (uint32_t*)at(ws, L.bitmap) : nullptr;
   int32_t* counts = mark ? (int32_t*)at(ws, L.counts) : nullptr;
-  // the bitmap and the counts are adjacent in the layout: one range to clear
-  const int64_t clear_words = (int64_t)(L.counts - L.bitmap) / 4 + c->num_experts;
+  moe::FusedDispatch none;
+  if (fd) fd->done = counts + c->num_experts;
+  // the bitmap and the counts (with the fused dispatch's counter after them) are adjacent in
+  // the layout: one range to clear
+  const int64_t clear_words = (int64_t)(L.counts - L.bitmap) / 4 + c->num_experts + 1;
   hipError_t e = moe::launch_router_logits(p, (const uint16_t*)x, rw, (int)T, c->hidden_size, c->num_experts,
                                            partial, bitmap, clear_words, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router logits launch");
   e = moe::launch_router_topk(partial, p.nsplit, (int)T, c->num_experts, bias, c->n_group, c->topk_group,
                               c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, bitmap,
-                              counts, s, tr);
+                              counts, fd ? *fd : none, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router top-k launch");
   return MOE_OK;
 }
@@ -333,9 +338,24 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);
   void* y = at(ws, L.y);
   if (tr && tr->events && tr->cap > 0 && tr->events[0]) (void)hipEventRecord(tr->events[0], s);
-  if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true)) != MOE_OK) return st;
-  if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
-    return st;
+  if (T <= moe::FUSED_DISPATCH_MAX_T) {
+    // few tokens: the top-k kernel's last workgroup finishes the dispatch (one launch fewer)
+    moe::FusedDispatch fd;
+    fd.counts_out = counts;
+    fd.offsets = offsets;
+    fd.sorted_token = sorted_token;
+    fd.inv_perm = inv;
+    fd.tile_prefix = (int32_t*)at(ws, L.tile_prefix);
+    fd.S = cfg->num_shared_experts;
+    fd.bm = moe::ffn_plan(T, cfg->num_experts_per_tok, cfg->num_experts, cfg->num_shared_experts,
+                          cfg->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                          cfg->hidden_size, cfg->moe_intermediate_size).bm;
+    if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true, &fd)) != MOE_OK) return st;
+  } else {
+    if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true)) != MOE_OK) return st;
+    if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
+      return st;
+  }
   if ((st = do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true)) != MOE_OK) return st;
   return do_combine(cfg, T, y, inv, wts, out, s, tr);
 }

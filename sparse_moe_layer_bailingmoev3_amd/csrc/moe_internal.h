@@ -39,9 +39,23 @@ size_t router_partial_bytes(int64_t T, int H, int E);
 hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const float* w, int T, int H,
                                 int E, float* partial, uint32_t* clear, int64_t clear_words, hipStream_t s,
                                 Tracer* tr = nullptr);
+// Dispatch finished inside the top-k kernel (few tokens): the last workgroup to finish, found
+// with a counter (`done`, zero before the launch), writes the offsets, the sorted tokens,
+// inv_perm, the expert counts and the FFN tile prefix from the complete bitmap and histogram.
+struct FusedDispatch {
+  int32_t* done = nullptr;  // null: no fused dispatch
+  int32_t* counts_out = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_token = nullptr;
+  int32_t* inv_perm = nullptr;
+  int32_t* tile_prefix = nullptr;  // optional
+  int S = 0, bm = 1;
+};
+constexpr int FUSED_DISPATCH_MAX_T = 256;
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G,
                               int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
-                              uint32_t* bitmap, int32_t* counts, hipStream_t s, Tracer* tr = nullptr);
+                              uint32_t* bitmap, int32_t* counts, const FusedDispatch& fd, hipStream_t s,
+                              Tracer* tr = nullptr);
 
 // ---- dispatch ----------------------------------------------------------------
 size_t dispatch_bitmap_words(int64_t T, int E);

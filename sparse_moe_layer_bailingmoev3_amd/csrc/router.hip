@@ -125,19 +125,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// One wave per token.  Lane l holds experts l*EPL .. l*EPL + EPL - 1, so a group of E/G
-// experts is 64/G consecutive lanes.
+// One token (one wave): the top-k of the routing walk-through page's sections 三.1-三.3.
 template <int EPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
-                                                          int T, int E, const float* __restrict__ bias, int G,
-                                                          int TG, int K, int norm, float scale,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w,
-                                                          uint32_t* __restrict__ bitmap, int words,
-                                                          int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+__device__ __forceinline__ void route_token(const float* __restrict__ partial, int nsplit, int T, int E,
+                                            const float* __restrict__ bias, int G, int TG, int K, int norm,
+                                            float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                            uint32_t* __restrict__ bitmap, int words, int32_t* __restrict__ counts,
+                                            int t, int lane) {
   const int e0 = lane * EPL;
 
   // logits: split partial sums added in split order
@@ -225,6 +219,109 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
+// The dispatch of the fused forward for few tokens, run by the last top-k workgroup to finish
+// (the one that brings `done` to the grid size): the same results as the dispatch kernels'
+// finish step.  Every workgroup first makes its top-k stores and bitmap/histogram atomics
+// visible (release fence before the counter), and the last one reads them after an acquire
+// fence, through loads that bypass the non-coherent L1.
+__device__ __forceinline__ int load_acq(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_acq(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, const int32_t* topk_idx,
+                                                   const uint32_t* bitmap, const int32_t* counts, int T, int K,
+                                                   int E, int words) {
+  __shared__ int last;
+  __shared__ int offs[1024 + 1];
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(fd.done, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    // exclusive scans of the expert counts and of their FFN tiles
+    const int per = (E + 63) / 64;
+    const int b = lane * per, en = min(E, b + per);
+    int sum = 0, tsum = 0;
+    for (int i = b; i < en; ++i) {
+      const int c = load_acq(counts + i);
+      sum += c;
+      tsum += (c + fd.bm - 1) / fd.bm;
+    }
+    int incl = sum, tincl = tsum;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(incl, m, 64), to = __shfl_up(tincl, m, 64);
+      if (lane >= m) {
+        incl += o;
+        tincl += to;
+      }
+    }
+    int run = incl - sum, trun = tincl - tsum;
+    for (int i = b; i < en; ++i) {
+      const int c = load_acq(counts + i);
+      offs[i] = run;
+      fd.offsets[i] = run;
+      fd.counts_out[i] = c;
+      if (fd.tile_prefix) fd.tile_prefix[i] = trun;
+      run += c;
+      trun += (c + fd.bm - 1) / fd.bm;
+    }
+    const int routed = __shfl(incl, 63, 64), trouted = __shfl(tincl, 63, 64);
+    if (lane == 0) {
+      offs[E] = routed;
+      fd.counts_out[E] = T * fd.S;
+      fd.offsets[E] = routed;
+      fd.offsets[E + 1] = routed + T * fd.S;
+      if (fd.tile_prefix) {
+        fd.tile_prefix[E] = trouted;
+        fd.tile_prefix[E + 1] = trouted + (fd.S ? (T + fd.bm - 1) / fd.bm : 0);
+      }
+    }
+  }
+  __syncthreads();
+  // each (token, slot): its position is the expert's offset plus the number of the expert's
+  // tokens before it (set bits of the expert's bitmap row below the token)
+  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+    const int t = p / K, e = load_acq(topk_idx + p);
+    if (e < 0 || e >= E) {
+      fd.inv_perm[p] = -1;
+      continue;
+    }
+    const uint32_t* row = bitmap + (size_t)e * words;
+    int rank = __popc(load_acq(row + (t >> 5)) & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(load_acq(row + w));
+    const int pos = offs[e] + rank;
+    fd.sorted_token[pos] = t;
+    fd.inv_perm[p] = pos;
+  }
+  if (fd.S)
+    for (int t = threadIdx.x; t < T; t += blockDim.x) fd.sorted_token[offs[E] + t] = t;
+}
+
+// One wave per token.  Lane l holds experts l*EPL .. l*EPL + EPL - 1, so a group of E/G
+// experts is 64/G consecutive lanes.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
+                                                          int T, int E, const float* __restrict__ bias, int G,
+                                                          int TG, int K, int norm, float scale,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w,
+                                                          uint32_t* __restrict__ bitmap, int words,
+                                                          int32_t* __restrict__ counts, FusedDispatch fd) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < T) route_token<EPL>(partial, nsplit, T, E, bias, G, TG, K, norm, scale, topk_idx, topk_w, bitmap, words,
+                              counts, t, lane);
+  if (fd.done) fused_dispatch_finish(fd, topk_idx, bitmap, counts, T, K, E, words);
+}
+
+
 int pick_router_mf(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8; }
 
 }  // namespace
@@ -285,13 +382,14 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
 
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G, int TG,
                               int K, int norm, float scale, int32_t* topk_idx, float* topk_w, uint32_t* bitmap,
-                              int32_t* counts, hipStream_t s, Tracer* tr) {
+                              int32_t* counts, const FusedDispatch& fd, hipStream_t s, Tracer* tr) {
+  if (fd.done && (!bitmap || T > FUSED_DISPATCH_MAX_T || E > 1024)) return hipErrorInvalidValue;
   const int words = (T + 31) / 32;
   dim3 grid((T + 3) / 4), block(256);
   const int epl = E / WAVE;
 #define MOE_TOPK(N)                                                                                          \
   hipLaunchKernelGGL(router_topk_kernel<N>, grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, norm, \
-                     scale, topk_idx, topk_w, bitmap, words, counts)
+                     scale, topk_idx, topk_w, bitmap, words, counts, fd)
   switch (epl) {
     case 1: MOE_TOPK(1); break;
     case 2: MOE_TOPK(2); break;
