@@ -31,6 +31,7 @@ struct RouterPlan {
   int rf;       // 16-expert blocks per wave (1 or 2)
   int nsplit;   // split of the hidden dimension (partial logits summed in order)
   int m_tiles, n_tiles;
+  bool kwaves;  // few tokens: 16 experts per workgroup, its 4 waves split the k range
 };
 RouterPlan router_plan(int64_t T, int H, int E);
 size_t router_partial_bytes(int64_t T, int H, int E);

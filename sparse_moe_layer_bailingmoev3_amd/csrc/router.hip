@@ -125,6 +125,101 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Few tokens: the same partial sums from more, shorter workgroups.  A workgroup owns 16
+// experts, tokens m0 .. m0 + 16*MF - 1 and one split of h; its 4 waves take consecutive
+// quarters of the split, issue all their loads at once (two 32-wide k steps per round), and
+// their sums are added through LDS in wave order.  Needs kchunk % 128 == 0.
+template <int MF>
+__global__ __launch_bounds__(256) void router_logits_kwaves_kernel(const uint16_t* __restrict__ x,
+                                                                   const float* __restrict__ w, int T, int H,
+                                                                   int E, int kchunk, float* __restrict__ partial,
+                                                                   uint32_t* __restrict__ clear,
+                                                                   int64_t clear_words) {
+  __shared__ floatx4 red[4][MF][64];
+  if (clear) {
+    const int64_t nth = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < clear_words;
+         i += nth)
+      clear[i] = 0u;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int n_tiles = E / 16;
+  const int nt = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
+  const int m0 = blockIdx.y * 16 * MF;
+  const int e_base = nt * 16;
+  const int kw = kchunk / 4;  // this wave's k range
+  const int k0 = split * kchunk + wave * kw;
+
+  const float* wr = w + (size_t)(e_base + r16) * H + k0 + q * 8;
+  const uint16_t* xr[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int t = min(m0 + mf * 16 + r16, T - 1);
+    xr[mf] = x + (size_t)t * H + k0 + q * 8;
+  }
+  floatx4 acc[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) acc[mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const float4 (&a)[2], const u32x4 (&xv)[MF]) {
+    const float v[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
+    u32x4 hi, mid, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h, m, l;
+      split3(v[2 * i], v[2 * i + 1], h, m, l);
+      hi[i] = h;
+      mid[i] = m;
+      lo[i] = l;
+    }
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      acc[mf] = mfma16(lo, xv[mf], acc[mf]);
+      acc[mf] = mfma16(mid, xv[mf], acc[mf]);
+      acc[mf] = mfma16(hi, xv[mf], acc[mf]);
+    }
+  };
+  for (int kk = 0; kk + 64 <= kw; kk += 64) {
+    float4 a[2][2];
+    u32x4 xv[2][MF];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      a[u][0] = *(const float4*)(wr + kk + 32 * u);
+      a[u][1] = *(const float4*)(wr + kk + 32 * u + 4);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) xv[u][mf] = *(const u32x4*)(xr[mf] + kk + 32 * u);
+    }
+    step(a[0], xv[0]);
+    step(a[1], xv[1]);
+  }
+  if (kw % 64) {  // one 32-wide step left
+    const int kk = kw - 32;
+    float4 a[2];
+    u32x4 xv[MF];
+    a[0] = *(const float4*)(wr + kk);
+    a[1] = *(const float4*)(wr + kk + 4);
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) xv[mf] = *(const u32x4*)(xr[mf] + kk);
+    step(a, xv);
+  }
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) red[wave][mf][lane] = acc[mf];
+  __syncthreads();
+  // lane holds token r16 of each fragment, experts 4q .. 4q+3; fragment mf is summed (waves
+  // 0, 1, 2, 3 in order) and stored by wave mf % 4
+  float* out = partial + (size_t)split * T * E;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    if (mf % 4 != wave) continue;
+    const int t = m0 + mf * 16 + r16;
+    if (t < T) {
+      const floatx4 s = ((red[0][mf][lane] + red[1][mf][lane]) + red[2][mf][lane]) + red[3][mf][lane];
+      *(float4*)(out + (size_t)t * E + e_base + 4 * q) = float4{s[0], s[1], s[2], s[3]};
+    }
+  }
+}
+
 // One token (one wave): the top-k of the routing walk-through page's sections 三.1-三.3.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ partial, int nsplit, int T, int E,
@@ -344,6 +439,23 @@ RouterPlan router_plan(int64_t T, int H, int E) {
     best = ns;
   }
   p.nsplit = best;
+  p.kwaves = false;
+  if (T <= 256 && p.m_tiles * p.n_tiles < 256 && E % 16 == 0) {
+    // few tokens: 16-expert workgroups whose waves split the k range (each wave's share a
+    // multiple of 32); the fewest splits (at most 10) that give ~256 workgroups.  (More
+    // tokens keep 64-expert workgroups, which read each token row E/64 times instead of E/16.)
+    int ks = 0;
+    for (int ns = 1; ns <= std::min(kb, 10); ++ns) {
+      if (kb % ns || (kb / ns) % 4) continue;
+      ks = ns;
+      if ((int64_t)p.m_tiles * (E / 16) * ns >= 256) break;
+    }
+    if (ks) {
+      p.kwaves = true;
+      p.nsplit = ks;
+      p.n_tiles = E / 16;
+    }
+  }
   return p;
 }
 
@@ -356,6 +468,22 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
                                 float* partial, uint32_t* clear, int64_t clear_words, hipStream_t s, Tracer* tr) {
   dim3 grid(p.n_tiles * p.nsplit, p.m_tiles), block(256);
   const int kchunk = H / p.nsplit;
+  if (p.kwaves) {
+    if (kchunk % 128 || E % 16) return hipErrorInvalidValue;
+#define MOE_RLK(M)                                                                                           \
+  hipLaunchKernelGGL((router_logits_kwaves_kernel<M>), grid, block, 0, s, x, w, T, H, E, kchunk, partial, clear, \
+                     clear_words)
+    switch (p.mf) {
+      case 1: MOE_RLK(1); break;
+      case 2: MOE_RLK(2); break;
+      case 4: MOE_RLK(4); break;
+      default: MOE_RLK(8); break;
+    }
+#undef MOE_RLK
+    hipError_t err = hipGetLastError();
+    if (tr) tr->mark("router_logits", s);
+    return err;
+  }
 #define MOE_RL(M, R)                                                                                         \
   hipLaunchKernelGGL((router_logits_kernel<M, R>), grid, block, 0, s, x, w, T, H, E, kchunk, partial, clear, \
                      clear_words)
