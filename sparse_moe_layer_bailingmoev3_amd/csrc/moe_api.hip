@@ -338,7 +338,8 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);
   void* y = at(ws, L.y);
   if (tr && tr->events && tr->cap > 0 && tr->events[0]) (void)hipEventRecord(tr->events[0], s);
-  if (T <= moe::FUSED_DISPATCH_MAX_T) {
+  if (T <= moe::FUSED_DISPATCH_MAX_T && T * cfg->num_experts_per_tok <= moe::FUSED_DISPATCH_MAX_PAIRS &&
+      cfg->num_experts <= moe::FUSED_DISPATCH_MAX_E) {
     // few tokens: the top-k kernel's last workgroup finishes the dispatch (one launch fewer)
     moe::FusedDispatch fd;
     fd.counts_out = counts;

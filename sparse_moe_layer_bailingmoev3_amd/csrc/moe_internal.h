@@ -42,7 +42,8 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
                                 Tracer* tr = nullptr);
 // Dispatch finished inside the top-k kernel (few tokens): the last workgroup to finish, found
 // with a counter (`done`, zero before the launch), writes the offsets, the sorted tokens,
-// inv_perm, the expert counts and the FFN tile prefix from the complete bitmap and histogram.
+// inv_perm, the expert counts and the FFN tile prefix from the complete topk_idx (bitmap and
+// histogram rebuilt in its LDS; the top-k workgroups then make no dispatch atomics).
 struct FusedDispatch {
   int32_t* done = nullptr;  // null: no fused dispatch
   int32_t* counts_out = nullptr;
@@ -53,6 +54,8 @@ struct FusedDispatch {
   int S = 0, bm = 1;
 };
 constexpr int FUSED_DISPATCH_MAX_T = 256;
+constexpr int FUSED_DISPATCH_MAX_PAIRS = 4096;  // tokens x slots
+constexpr int FUSED_DISPATCH_MAX_E = 1024;
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G,
                               int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
                               uint32_t* bitmap, int32_t* counts, const FusedDispatch& fd, hipStream_t s,

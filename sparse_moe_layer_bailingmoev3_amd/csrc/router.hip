@@ -316,35 +316,56 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
 
 // The dispatch of the fused forward for few tokens, run by the last top-k workgroup to finish
 // (the one that brings `done` to the grid size): the same results as the dispatch kernels'
-// finish step.  Every workgroup first makes its top-k stores and bitmap/histogram atomics
-// visible (release fence before the counter), and the last one reads them after an acquire
-// fence, through loads that bypass the non-coherent L1.
+// finish step.  Every workgroup first makes its top-k stores visible (release fence before
+// the counter); the last one reads all of topk_idx once after an acquire fence, through
+// loads that bypass the non-coherent L1, and builds the bitmap and the histogram in LDS.
 __device__ __forceinline__ int load_acq(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_acq(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
-__device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, const int32_t* topk_idx,
-                                                   const uint32_t* bitmap, const int32_t* counts, int T, int K,
-                                                   int E, int words) {
+constexpr int FD_WORDS = FUSED_DISPATCH_MAX_T / 32;                // bitmap words per expert
+constexpr int FD_PER_THREAD = FUSED_DISPATCH_MAX_PAIRS / 256;      // (token, slot) pairs per thread
+
+__device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, const int32_t* topk_idx, int T,
+                                                   int K, int E) {
   __shared__ int last;
-  __shared__ int offs[1024 + 1];
+  __shared__ int offs[FUSED_DISPATCH_MAX_E + 1];
+  __shared__ int cnt[FUSED_DISPATCH_MAX_E];
+  __shared__ uint32_t bits[FUSED_DISPATCH_MAX_E * FD_WORDS];
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) last = atomicAdd(fd.done, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!last) return;
   __threadfence();
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
+  const int tid = threadIdx.x, TK = T * K;
+  int ev[FD_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < FD_PER_THREAD; ++u) {
+    const int p = tid + u * 256;
+    ev[u] = p < TK ? load_acq(topk_idx + p) : -1;
+  }
+  for (int i = tid; i < E; i += 256) cnt[i] = 0;
+  for (int i = tid; i < E * FD_WORDS; i += 256) bits[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < FD_PER_THREAD; ++u) {
+    const int p = tid + u * 256, e = ev[u];
+    if (p < TK && e >= 0 && e < E) {
+      const int t = p / K;
+      atomicOr(&bits[e * FD_WORDS + (t >> 5)], 1u << (t & 31));
+      atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  if (tid < 64) {
     // exclusive scans of the expert counts and of their FFN tiles
     const int per = (E + 63) / 64;
     const int b = lane * per, en = min(E, b + per);
     int sum = 0, tsum = 0;
     for (int i = b; i < en; ++i) {
-      const int c = load_acq(counts + i);
+      const int c = cnt[i];
       sum += c;
       tsum += (c + fd.bm - 1) / fd.bm;
     }
@@ -359,7 +380,7 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
     }
     int run = incl - sum, trun = tincl - tsum;
     for (int i = b; i < en; ++i) {
-      const int c = load_acq(counts + i);
+      const int c = cnt[i];
       offs[i] = run;
       fd.offsets[i] = run;
       fd.counts_out[i] = c;
@@ -382,26 +403,29 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
   __syncthreads();
   // each (token, slot): its position is the expert's offset plus the number of the expert's
   // tokens before it (set bits of the expert's bitmap row below the token)
-  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
-    const int t = p / K, e = load_acq(topk_idx + p);
+#pragma unroll
+  for (int u = 0; u < FD_PER_THREAD; ++u) {
+    const int p = tid + u * 256, e = ev[u];
+    if (p >= TK) continue;
     if (e < 0 || e >= E) {
       fd.inv_perm[p] = -1;
       continue;
     }
-    const uint32_t* row = bitmap + (size_t)e * words;
-    int rank = __popc(load_acq(row + (t >> 5)) & ((1u << (t & 31)) - 1u));
-    for (int w = 0; w < (t >> 5); ++w) rank += __popc(load_acq(row + w));
+    const int t = p / K;
+    const uint32_t* row = bits + e * FD_WORDS;
+    int rank = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
     const int pos = offs[e] + rank;
     fd.sorted_token[pos] = t;
     fd.inv_perm[p] = pos;
   }
   if (fd.S)
-    for (int t = threadIdx.x; t < T; t += blockDim.x) fd.sorted_token[offs[E] + t] = t;
+    for (int t = tid; t < T; t += 256) fd.sorted_token[offs[E] + t] = t;
 }
 
 // One wave per token.  Lane l holds experts l*EPL .. l*EPL + EPL - 1, so a group of E/G
 // experts is 64/G consecutive lanes.
-template <int EPL>
+template <int EPL, bool FUSED>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
                                                           int T, int E, const float* __restrict__ bias, int G,
                                                           int TG, int K, int norm, float scale,
@@ -411,9 +435,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int32_t* __restrict__ counts, FusedDispatch fd) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t < T) route_token<EPL>(partial, nsplit, T, E, bias, G, TG, K, norm, scale, topk_idx, topk_w, bitmap, words,
-                              counts, t, lane);
-  if (fd.done) fused_dispatch_finish(fd, topk_idx, bitmap, counts, T, K, E, words);
+  // the fused dispatch builds its bitmap and histogram from topk_idx itself
+  if (t < T) route_token<EPL>(partial, nsplit, T, E, bias, G, TG, K, norm, scale, topk_idx, topk_w,
+                              FUSED ? nullptr : bitmap, words, counts, t, lane);
+  if constexpr (FUSED) fused_dispatch_finish(fd, topk_idx, T, K, E);
 }
 
 
@@ -511,13 +536,18 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G, int TG,
                               int K, int norm, float scale, int32_t* topk_idx, float* topk_w, uint32_t* bitmap,
                               int32_t* counts, const FusedDispatch& fd, hipStream_t s, Tracer* tr) {
-  if (fd.done && (!bitmap || T > FUSED_DISPATCH_MAX_T || E > 1024)) return hipErrorInvalidValue;
+  if (fd.done && (T > FUSED_DISPATCH_MAX_T || (int64_t)T * K > FUSED_DISPATCH_MAX_PAIRS || E > FUSED_DISPATCH_MAX_E))
+    return hipErrorInvalidValue;
   const int words = (T + 31) / 32;
   dim3 grid((T + 3) / 4), block(256);
   const int epl = E / WAVE;
-#define MOE_TOPK(N)                                                                                          \
-  hipLaunchKernelGGL(router_topk_kernel<N>, grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, norm, \
-                     scale, topk_idx, topk_w, bitmap, words, counts, fd)
+#define MOE_TOPK(N)                                                                                         \
+  if (fd.done)                                                                                              \
+    hipLaunchKernelGGL((router_topk_kernel<N, true>), grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, \
+                       norm, scale, topk_idx, topk_w, bitmap, words, counts, fd);                           \
+  else                                                                                                      \
+    hipLaunchKernelGGL((router_topk_kernel<N, false>), grid, block, 0, s, partial, nsplit, T, E, bias, G, TG,   \
+                       K, norm, scale, topk_idx, topk_w, bitmap, words, counts, fd)
   switch (epl) {
     case 1: MOE_TOPK(1); break;
     case 2: MOE_TOPK(2); break;

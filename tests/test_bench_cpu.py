@@ -67,7 +67,9 @@ def test_symbols_map_to_steps():
     assert bench._step("ffn_tile_kernel<0, 8, 2, 3>") == "expert_gate_up"
     assert bench._step("ffn_tile_kernel<1, 16, 2, 3>") == "expert_down"
     assert bench._step("ffn_kernel<8, 1, 8, 4, 1, 1>") == "expert_down"
-    assert bench._step("router_topk_kernel<8>") == "router_topk"
+    assert bench._step("router_topk_kernel<8, true>") == "router_topk"
+    assert bench._step("router_logits_kwaves_kernel<4>") == "router_logits"
+    assert bench._step("router_logits_kernel<8, 2>") == "router_logits"
     assert bench._step("something_else") is None
 
 
