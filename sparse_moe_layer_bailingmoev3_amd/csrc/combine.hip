@@ -10,7 +10,11 @@ namespace moe {
 
 namespace {
 
-// one workgroup per token; each thread owns 8 consecutive hidden values (16 bytes)
+// one workgroup per token; each thread owns 8 consecutive hidden values (16 bytes).  The
+// rows of 8 slots are loaded in one batch (a slot without a row loads row 0 and is skipped
+// in the sum), so a token costs one round trip per 8 slots instead of one per slot.
+constexpr int CB = 8;
+
 __global__ __launch_bounds__(512) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int T, int K, int H, int S,
                                                       uint16_t* __restrict__ out) {
@@ -20,32 +24,51 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* __restrict__ 
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int p = inv[(size_t)t * K + k];
-      if (p < 0) continue;
-      const float wk = w[(size_t)t * K + k];
-      const float4 v0 = *(const float4*)(y + (size_t)p * H + c);
-      const float4 v1 = *(const float4*)(y + (size_t)p * H + c + 4);
-      acc[0] = fmaf(wk, v0.x, acc[0]);
-      acc[1] = fmaf(wk, v0.y, acc[1]);
-      acc[2] = fmaf(wk, v0.z, acc[2]);
-      acc[3] = fmaf(wk, v0.w, acc[3]);
-      acc[4] = fmaf(wk, v1.x, acc[4]);
-      acc[5] = fmaf(wk, v1.y, acc[5]);
-      acc[6] = fmaf(wk, v1.z, acc[6]);
-      acc[7] = fmaf(wk, v1.w, acc[7]);
+    // the shared expert's row does not depend on the slot indices: load it first
+    float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if (S) {
+      s0 = *(const float4*)(y + (size_t)shared_row * H + c);
+      s1 = *(const float4*)(y + (size_t)shared_row * H + c + 4);
+    }
+    for (int k0 = 0; k0 < K; k0 += CB) {
+      // slot indices and weights read unconditionally (clamped to the last slot) so that
+      // they go out as one batch
+      int p[CB];
+      float wt[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int k = min(k0 + u, K - 1);
+        p[u] = inv[(size_t)t * K + k];
+        wt[u] = w[(size_t)t * K + k];
+      }
+      float4 v[CB][2];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (k0 + u >= K) p[u] = -1;
+        const float* row = y + (size_t)(p[u] < 0 ? 0 : p[u]) * H + c;
+        v[u][0] = *(const float4*)row;
+        v[u][1] = *(const float4*)(row + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        // a skipped slot keeps the sum as it is (a select, not a branch, so that the weight
+        // loads stay in the batch)
+        const float wk = wt[u];
+        const bool use = p[u] >= 0;
+        const float r[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = use ? fmaf(wk, r[i], acc[i]) : acc[i];
+      }
     }
     if (S) {
-      const float4 v0 = *(const float4*)(y + (size_t)shared_row * H + c);
-      const float4 v1 = *(const float4*)(y + (size_t)shared_row * H + c + 4);
-      acc[0] += v0.x;
-      acc[1] += v0.y;
-      acc[2] += v0.z;
-      acc[3] += v0.w;
-      acc[4] += v1.x;
-      acc[5] += v1.y;
-      acc[6] += v1.z;
-      acc[7] += v1.w;
+      acc[0] += s0.x;
+      acc[1] += s0.y;
+      acc[2] += s0.z;
+      acc[3] += s0.w;
+      acc[4] += s1.x;
+      acc[5] += s1.y;
+      acc[6] += s1.z;
+      acc[7] += s1.w;
     }
     u32x4 o;
 #pragma unroll
