@@ -169,21 +169,20 @@ def measure(shape, d, steps, warmup, hip):
     dom = max(("expert_gate_up", "expert_down"), key=lambda n: kmean.get(n, 0.0))
     k = names.index(dom)
 
-    # timed region: `steps` forwards, each with the two events around its dominant kernel only
-    timed = [[None] * (len(names) + 1) for _ in range(steps)]
-    for s in range(steps):
-        timed[s][k], timed[s][k + 1] = hip.event(), hip.event()
+    # timed region: `steps` forwards; in each, the dominant kernel is timed by two events bound
+    # to its own dispatch (moe_forward_timed), which add no packets to the queue
+    timed = [(hip.event(), hip.event()) for _ in range(steps)]
     t_start, t_end = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(t_start, stream)
     for s in range(steps):
-        moe.moe_forward_traced(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, timed[s])
+        moe.moe_forward_timed(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, ws, k, *timed[s])
     hip.record(t_end, stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = hip.elapsed_ms(t_start, t_end) / steps
-    dom_ms = float(np.mean([hip.elapsed_ms(timed[s][k], timed[s][k + 1]) for s in range(steps)]))
+    dom_ms = float(np.mean([hip.elapsed_ms(*timed[s]) for s in range(steps)]))
     # routing of the last step (for algorithmic bytes)
     moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
     torch.cuda.synchronize()
@@ -192,8 +191,8 @@ def measure(shape, d, steps, warmup, hip):
 
 
 def roofline(shape, r, workload=None):
-    """Roofline of the dominant kernel (the longer of gate/up and down), timed by the two
-    events around it in every step of the timed region.
+    """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
+    bound to its dispatch in every step of the timed region.
 
     Algorithmic bytes per launch (what the method has to move, once):
       expert_gate_up: (touched routed experts + shared) * 2*I*H weights in their storage

@@ -171,6 +171,18 @@ moe_status_t moe_forward_traced(const moe_config_t* cfg, int64_t T, const void* 
                                 void* ws, size_t ws_bytes, void* stream, void* const* events,
                                 int32_t max_events, const char** kernel_names, int32_t* n_kernels);
 
+/* moe_forward with one kernel timed by events bound to its own dispatch (the AMD launch
+ * extension hipExtLaunchKernel): start_event and stop_event (hipEvent_t created by the caller,
+ * passed as void*) take that kernel's start and end times, and no other queue packets are
+ * added, so the step runs as fast as moe_forward (same results).  kernel_index counts the
+ * kernels in the order moe_forward_traced names them (0 = the first); a step that launches
+ * several kernels under one name is timed by its first.  Returns MOE_ERR_INVALID_ARG (after
+ * running the layer) if the forward launched no kernel with that index. */
+moe_status_t moe_forward_timed(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                               const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                               void* ws, size_t ws_bytes, void* stream, int32_t kernel_index,
+                               void* start_event, void* stop_event);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status_t status);
 

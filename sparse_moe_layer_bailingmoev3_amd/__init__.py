@@ -17,14 +17,14 @@ from typing import Optional
 
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
-           "moe_status_string",
+           "moe_forward_timed", "moe_status_string",
            "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "EXPORTED_SYMBOLS"]
 
 MOE_WEIGHTS_BF16 = 0
 MOE_WEIGHTS_MXFP4 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                    "moe_forward", "moe_forward_traced", "moe_status_string", "moe_last_error")
+                    "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_status_string", "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -87,6 +87,7 @@ def load_library():
         "moe_forward": [C, I64, P, P, P, W, P, P, P, P, P, SZ, P],
         "moe_forward_traced": [C, I64, P, P, P, W, P, P, SZ, P, ctypes.POINTER(P), ctypes.c_int32,
                                ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int32)],
+        "moe_forward_timed": [C, I64, P, P, P, W, P, P, SZ, P, ctypes.c_int32, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -181,3 +182,13 @@ def moe_forward_traced(cfg, T, x, router_w, expert_bias, weights: MoEExpertWeigh
                                              ctypes.byref(weights.struct), _ptr(out), p, n, _stream(stream), ev,
                                              len(events), names, ctypes.byref(nk)))
     return [names[i].decode() for i in range(nk.value)]
+
+
+def moe_forward_timed(cfg, T, x, router_w, expert_bias, weights: MoEExpertWeights, out, ws, kernel_index,
+                      start_event, stop_event, stream=None):
+    """moe_forward with kernel `kernel_index` (its position in moe_forward_traced's list) timed
+    by two raw hipEvent_t handles bound to its dispatch; adds nothing else to the queue."""
+    p, n = _ws(ws)
+    _check(load_library().moe_forward_timed(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
+                                            ctypes.byref(weights.struct), _ptr(out), p, n, _stream(stream),
+                                            kernel_index, start_event, stop_event))

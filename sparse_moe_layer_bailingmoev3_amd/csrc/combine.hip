@@ -83,7 +83,7 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const 
                           int S, uint16_t* out, hipStream_t s, Tracer* tr) {
   int threads = ((H / 8 + 63) / 64) * 64;
   threads = std::min(threads, 512);
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(threads), 0, s, y_sorted, inv_perm, topk_w, T, K, H, S, out);
+  launch(tr, combine_kernel, dim3(T), dim3(threads), s, y_sorted, inv_perm, topk_w, T, K, H, S, out);
   hipError_t err = hipGetLastError();
   if (tr) tr->mark("combine", s);
   return err;

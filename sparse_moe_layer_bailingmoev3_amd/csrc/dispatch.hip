@@ -161,17 +161,17 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, 
   if (!marked) {
     const size_t nbits = (size_t)E * words;
     int zb = (int)std::min<size_t>((nbits + 255) / 256, 1024);
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(zb), dim3(256), 0, s, bitmap, nbits, 0u);
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, s, (uint32_t*)counts, (size_t)E, 0u);
+    launch(tr, fill_u32_kernel, dim3(zb), dim3(256), s, bitmap, nbits, 0u);
+    launch(tr, fill_u32_kernel, dim3(1), dim3(256), s, (uint32_t*)counts, (size_t)E, 0u);
     if (tr) tr->mark("dispatch_clear", s);
     const int64_t pairs = (int64_t)T * K;
-    hipLaunchKernelGGL(dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, topk_idx, T, K,
+    launch(tr, dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), s, topk_idx, T, K,
                        E, words, bitmap, counts, inv_perm);
     if (tr) tr->mark("dispatch_mark", s);
   }
   const int nchunks = (words + WAVE - 1) / WAVE;
   const int eb = (E * nchunks + 1 + 3) / 4;
-  hipLaunchKernelGGL(dispatch_finish_kernel, dim3(eb), dim3(256), 0, s, bitmap, counts, counts_out, topk_idx, T, K, E,
+  launch(tr, dispatch_finish_kernel, dim3(eb), dim3(256), s, bitmap, counts, counts_out, topk_idx, T, K, E,
                      words, S, offsets, sorted_token, inv_perm, tile_prefix, bm);
   if (tr) tr->mark("dispatch_finish", s);
   return hipGetLastError();

@@ -419,7 +419,7 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   int64_t work = max_tiles * (a.bm_list / (16 * MF)) * a.ngroups;
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT>), dim3((unsigned)grid), dim3(C::NW * 64), 0, s, a);
+  launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
   hipError_t err = hipGetLastError();
   if (tr) tr->mark(MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
   return err;
@@ -476,7 +476,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   hipError_t err = hipSuccess;
   if (p.tiles) {
     if (!tiles_ready) {
-      hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
+      launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix);
       err = hipGetLastError();
       if (tr) tr->mark("expert_tiles", s);
       if (err != hipSuccess) return err;
@@ -485,7 +485,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                                    shared_limit, h_hi, h_lo, y, s, tr);
   }
   if (!tiles_ready) {
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, E + S, p.bm, tile_prefix);
+    launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix);
     err = hipGetLastError();
     if (tr) tr->mark("expert_tiles", s);
   }

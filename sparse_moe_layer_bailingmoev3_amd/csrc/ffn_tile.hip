@@ -441,16 +441,14 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   constexpr int GU_SUBS = T_LIST_BM / (T_NW * GU_TPW * 16), DN_SUBS = T_LIST_BM / (T_NW * DN_TPW * 16);
   int64_t g = std::min(grid_max, (max_tiles * GU_SUBS * gu.ngroups + 7) / 8 * 8);
   if (g > 0) {
-    hipLaunchKernelGGL((ffn_tile_kernel<TM_GATEUP, GU_RFR, GU_TPW, GU_NST>), dim3((unsigned)g), dim3(T_NW * 64), 0,
-                       s, gu);
+    launch(tr, ffn_tile_kernel<TM_GATEUP, GU_RFR, GU_TPW, GU_NST>, dim3((unsigned)g), dim3(T_NW * 64), s, gu);
     hipError_t err = hipGetLastError();
     if (tr) tr->mark("expert_gate_up", s);
     if (err != hipSuccess) return err;
   }
   g = std::min(grid_max, (max_tiles * DN_SUBS * dn.ngroups + 7) / 8 * 8);
   if (g > 0) {
-    hipLaunchKernelGGL((ffn_tile_kernel<TM_DOWN, DN_RFR, DN_TPW, DN_NST>), dim3((unsigned)g), dim3(T_NW * 64), 0,
-                       s, dn);
+    launch(tr, ffn_tile_kernel<TM_DOWN, DN_RFR, DN_TPW, DN_NST>, dim3((unsigned)g), dim3(T_NW * 64), s, dn);
     hipError_t err = hipGetLastError();
     if (tr) tr->mark("expert_down", s);
     if (err != hipSuccess) return err;

@@ -389,4 +389,21 @@ moe_status_t moe_forward_traced(const moe_config_t* cfg, int64_t T, const void* 
   return st;
 }
 
+moe_status_t moe_forward_timed(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                               const float* expert_bias, const moe_expert_weights_t* weights, void* out, void* ws,
+                               size_t ws_bytes, void* stream, int32_t kernel_index, void* start_event,
+                               void* stop_event) {
+  if (!start_event || !stop_event || kernel_index < 0)
+    return fail(MOE_ERR_INVALID_ARG, "start_event and stop_event are required, kernel_index >= 0");
+  moe::Tracer tr;
+  tr.tindex = kernel_index;
+  tr.tstart = (hipEvent_t)start_event;
+  tr.tstop = (hipEvent_t)stop_event;
+  moe_status_t st = forward_impl(cfg, T, x, router_w, expert_bias, weights, out, nullptr, nullptr, nullptr, ws,
+                                 ws_bytes, stream, &tr);
+  if (st == MOE_OK && !tr.timed)
+    return fail(MOE_ERR_INVALID_ARG, "kernel_index %d: the forward launched %d kernels", kernel_index, tr.n);
+  return st;
+}
+
 }  // extern "C"

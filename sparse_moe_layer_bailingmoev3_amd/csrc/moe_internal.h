@@ -1,5 +1,6 @@
 // Internal launch interface between the C-ABI host layer and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,12 +11,16 @@ enum { FMT_BF16 = 0, FMT_MXFP4 = 1 };
 
 // Optional per-kernel event trace: events[0] is recorded before the first launch,
 // events[i+1] right after the i-th kernel (a NULL slot records nothing); names[i] names that
-// kernel.
+// kernel.  Independently, kernel `tindex` can be timed by events bound to its own dispatch
+// (tstart, tstop: no extra queue packets, so the step runs as it does untraced).
 struct Tracer {
   hipEvent_t* events = nullptr;
   const char** names = nullptr;
   int cap = 0;  // number of events available
   int n = 0;    // kernels launched so far
+  int tindex = -1;
+  hipEvent_t tstart = nullptr, tstop = nullptr;
+  bool timed = false;  // the timed kernel was launched
   void mark(const char* name, hipStream_t s) {
     if (events && n + 1 < cap) {
       if (events[n + 1]) (void)hipEventRecord(events[n + 1], s);
@@ -24,6 +29,19 @@ struct Tracer {
     ++n;
   }
 };
+
+// Every kernel of the library is launched through here: the kernel of step `tr->n` gets the
+// timing events bound to its dispatch when the tracer asks for them (the first launch of a
+// step that launches several).  Errors are read by the caller with hipGetLastError.
+template <typename... KArgs, typename... Args>
+void launch(Tracer* tr, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  if (tr && tr->tstart && !tr->timed && tr->tindex == tr->n) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, tr->tstart, tr->tstop, 0, args...);
+    tr->timed = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
 
 // ---- router ------------------------------------------------------------------
 struct RouterPlan {

@@ -496,7 +496,7 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
   if (p.kwaves) {
     if (kchunk % 128 || E % 16) return hipErrorInvalidValue;
 #define MOE_RLK(M)                                                                                           \
-  hipLaunchKernelGGL((router_logits_kwaves_kernel<M>), grid, block, 0, s, x, w, T, H, E, kchunk, partial, clear, \
+  launch(tr, router_logits_kwaves_kernel<M>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, \
                      clear_words)
     switch (p.mf) {
       case 1: MOE_RLK(1); break;
@@ -510,7 +510,7 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
     return err;
   }
 #define MOE_RL(M, R)                                                                                         \
-  hipLaunchKernelGGL((router_logits_kernel<M, R>), grid, block, 0, s, x, w, T, H, E, kchunk, partial, clear, \
+  launch(tr, router_logits_kernel<M, R>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, \
                      clear_words)
   if (p.rf == 2) {
     switch (p.mf) {
@@ -543,10 +543,10 @@ hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, co
   const int epl = E / WAVE;
 #define MOE_TOPK(N)                                                                                         \
   if (fd.done)                                                                                              \
-    hipLaunchKernelGGL((router_topk_kernel<N, true>), grid, block, 0, s, partial, nsplit, T, E, bias, G, TG, K, \
+    launch(tr, router_topk_kernel<N, true>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, \
                        norm, scale, topk_idx, topk_w, bitmap, words, counts, fd);                           \
   else                                                                                                      \
-    hipLaunchKernelGGL((router_topk_kernel<N, false>), grid, block, 0, s, partial, nsplit, T, E, bias, G, TG,   \
+    launch(tr, router_topk_kernel<N, false>, grid, block, s, partial, nsplit, T, E, bias, G, TG,   \
                        K, norm, scale, topk_idx, topk_w, bitmap, words, counts, fd)
   switch (epl) {
     case 1: MOE_TOPK(1); break;

@@ -197,6 +197,53 @@ def test_determinism_tiny():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
+@pytest.mark.parametrize("T", [40, 700])
+def test_traced_and_timed_forwards_match_forward(T):
+    """The profiling entry points compute the same layer, bit for bit; every kernel of the
+    step can be timed by events bound to its dispatch, and an index past the last kernel is
+    an error (after the layer ran)."""
+    import ctypes
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    c = host_case(CONFIGS["tiny"], seed=11, T=T)
+    dev = DeviceCase(c)
+    say(f"[gpu] moe_forward / moe_forward_traced / moe_forward_timed, tiny T={T}")
+    ref = dev.forward()[0].clone()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+
+    def event():
+        ev = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    out = torch.empty_like(ref)
+    events = [event() for _ in range(16)]
+    names = moe.moe_forward_traced(dev.cfg, T, dev.x, dev.router_w, dev.bias, dev.weights, out, dev.ws, events)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert names[0] == "router_logits" and names[-1] == "combine" and "expert_gate_up" in names
+    for k, name in enumerate(names):
+        out.zero_()
+        a, b = event(), event()
+        moe.moe_forward_timed(dev.cfg, T, dev.x, dev.router_w, dev.bias, dev.weights, out, dev.ws, k, a, b)
+        torch.cuda.synchronize()
+        ms = elapsed(a, b)
+        say(f"      kernel {k} {name}: {ms * 1e3:.1f} us")
+        assert 0.0 < ms < 1000.0
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    a, b = event(), event()
+    with pytest.raises(moe.MoEError):
+        moe.moe_forward_timed(dev.cfg, T, dev.x, dev.router_w, dev.bias, dev.weights, out, dev.ws, len(names), a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------------
 # adversarial fixtures (tiny layer)
 # ----------------------------------------------------------------------------------
