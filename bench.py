@@ -282,7 +282,8 @@ SYMBOL_STEPS = [(r"^ffn_tile_kernel<0,", "expert_gate_up"), (r"^ffn_tile_kernel<
                 (r"^ffn_kernel<\d+, \d+, \d+, \d+, 1,", "expert_down"),
                 (r"^router_logits_(kwaves_)?kernel", "router_logits"), (r"^router_topk_kernel", "router_topk"),
                 (r"^fill_u32_kernel", "dispatch_clear"), (r"^dispatch_mark_kernel", "dispatch_mark"),
-                (r"^dispatch_finish_kernel", "dispatch_finish"), (r"^tile_prefix_kernel", "expert_tiles"),
+                (r"^dispatch_finish_kernel", "dispatch_finish"), (r"^dispatch_count_kernel", "dispatch_count"),
+                (r"^tile_prefix_kernel", "expert_tiles"),
                 (r"^combine_kernel", "combine"), (r"^__amd_rocclr_copyBuffer", "copy")]
 
 

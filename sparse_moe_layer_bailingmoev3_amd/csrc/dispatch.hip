@@ -37,6 +37,20 @@ __global__ void dispatch_mark_kernel(const int32_t* __restrict__ topk_idx, int T
   }
 }
 
+// marked bitmap (no expert twice for a token): counts[e] = set bits of row e, one wave per row
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __restrict__ bitmap, int words, int E,
+                                                             int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const uint32_t* row = bitmap + (size_t)e * words;
+  int c = 0;
+  for (int w = lane; w < words; w += WAVE) c += __popc(row[w]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, WAVE);
+  if (lane == 0) counts[e] = c;
+}
+
 // sum of v[0 .. n) over one wave (lane-strided)
 __device__ __forceinline__ int wave_sum_prefix(const int32_t* __restrict__ v, int n, int lane) {
   int c = 0;
@@ -165,14 +179,17 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, 
     launch(tr, fill_u32_kernel, dim3(1), dim3(256), s, (uint32_t*)counts, (size_t)E, 0u);
     if (tr) tr->mark("dispatch_clear", s);
     const int64_t pairs = (int64_t)T * K;
-    launch(tr, dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), s, topk_idx, T, K,
-                       E, words, bitmap, counts, inv_perm);
+    launch(tr, dispatch_mark_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), s, topk_idx, T, K, E,
+           words, bitmap, counts, inv_perm);
     if (tr) tr->mark("dispatch_mark", s);
+  } else {
+    launch(tr, dispatch_count_kernel, dim3((E + 3) / 4), dim3(256), s, (const uint32_t*)bitmap, words, E, counts);
+    if (tr) tr->mark("dispatch_count", s);
   }
   const int nchunks = (words + WAVE - 1) / WAVE;
   const int eb = (E * nchunks + 1 + 3) / 4;
-  launch(tr, dispatch_finish_kernel, dim3(eb), dim3(256), s, bitmap, counts, counts_out, topk_idx, T, K, E,
-                     words, S, offsets, sorted_token, inv_perm, tile_prefix, bm);
+  launch(tr, dispatch_finish_kernel, dim3(eb), dim3(256), s, bitmap, counts, counts_out, topk_idx, T, K, E, words,
+         S, offsets, sorted_token, inv_perm, tile_prefix, bm);
   if (tr) tr->mark("dispatch_finish", s);
   return hipGetLastError();
 }

@@ -170,15 +170,16 @@ moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const flo
   hipError_t e = moe::launch_router_logits(p, (const uint16_t*)x, rw, (int)T, c->hidden_size, c->num_experts,
                                            partial, bitmap, clear_words, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router logits launch");
+  // the histogram is counted from the bitmap by the dispatch (no histogram atomics here)
   e = moe::launch_router_topk(partial, p.nsplit, (int)T, c->num_experts, bias, c->n_group, c->topk_group,
                               c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, bitmap,
-                              counts, fd ? *fd : none, s, tr);
+                              nullptr, fd ? *fd : none, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router top-k launch");
   return MOE_OK;
 }
 
-// marked: the router already filled the bitmap and the workspace histogram; counts are
-// then copied to `counts` by the finish kernel.  with_tiles: also write the FFN tile prefix.
+// marked: the router already filled the bitmap; the workspace histogram is counted from it
+// and copied to `counts` by the finish kernel.  with_tiles: also write the FFN tile prefix.
 moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_token, int32_t* inv_perm, const Layout& L, void* ws, hipStream_t s,
                          moe::Tracer* tr = nullptr, bool marked = false, bool with_tiles = false) {

@@ -81,10 +81,11 @@ hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, co
 
 // ---- dispatch ----------------------------------------------------------------
 size_t dispatch_bitmap_words(int64_t T, int E);
-// marked: the bitmap and counts were already filled by the router's top-k kernel (and
-// cleared by its logits kernel).  tile_prefix (optional): tiles of bm positions per expert.
-// counts: the histogram (cleared and filled here unless marked); counts_out receives a copy
-// plus the shared expert's entry (may equal counts)
+// marked: the bitmap was already filled by the router's top-k kernel (and cleared by its
+// logits kernel), which lists an expert at most once per token, so the histogram is the
+// popcount of each bitmap row.  tile_prefix (optional): tiles of bm positions per expert.
+// counts: the histogram (filled here); counts_out receives a copy plus the shared expert's
+// entry (may equal counts)
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, uint32_t* bitmap,
                            int32_t* counts, int32_t* counts_out, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
                            bool marked, int32_t* tile_prefix, int bm, hipStream_t s, Tracer* tr = nullptr);

@@ -306,10 +306,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
     topk_idx[(size_t)t * K + pos] = my_idx;
     topk_w[(size_t)t * K + pos] = wv;
     if (bitmap) {
-      // dispatch: one bit per (expert, token) and the expert histogram (integer atomics,
-      // so the final values do not depend on their order)
+      // dispatch: one bit per (expert, token) (an integer atomic, so the final bitmap does
+      // not depend on the order); the histogram is added here only if asked for; otherwise
+      // it is the popcount of the bitmap rows (one atomic per pair on 512 counters
+      // serialises: 30 us of the top-k kernel at 8192 tokens, 100 us on skewed routing)
       atomicOr(&bitmap[(size_t)my_idx * words + (t >> 5)], 1u << (t & 31));
-      atomicAdd(&counts[my_idx], 1);
+      if (counts) atomicAdd(&counts[my_idx], 1);
     }
   }
 }
@@ -495,9 +497,8 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
   const int kchunk = H / p.nsplit;
   if (p.kwaves) {
     if (kchunk % 128 || E % 16) return hipErrorInvalidValue;
-#define MOE_RLK(M)                                                                                           \
-  launch(tr, router_logits_kwaves_kernel<M>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, \
-                     clear_words)
+#define MOE_RLK(M) \
+  launch(tr, router_logits_kwaves_kernel<M>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, clear_words)
     switch (p.mf) {
       case 1: MOE_RLK(1); break;
       case 2: MOE_RLK(2); break;
@@ -509,9 +510,8 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
     if (tr) tr->mark("router_logits", s);
     return err;
   }
-#define MOE_RL(M, R)                                                                                         \
-  launch(tr, router_logits_kernel<M, R>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, \
-                     clear_words)
+#define MOE_RL(M, R) \
+  launch(tr, router_logits_kernel<M, R>, grid, block, s, x, w, T, H, E, kchunk, partial, clear, clear_words)
   if (p.rf == 2) {
     switch (p.mf) {
       case 1: MOE_RL(1, 2); break;
@@ -541,13 +541,13 @@ hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, co
   const int words = (T + 31) / 32;
   dim3 grid((T + 3) / 4), block(256);
   const int epl = E / WAVE;
-#define MOE_TOPK(N)                                                                                         \
-  if (fd.done)                                                                                              \
-    launch(tr, router_topk_kernel<N, true>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, \
-                       norm, scale, topk_idx, topk_w, bitmap, words, counts, fd);                           \
-  else                                                                                                      \
-    launch(tr, router_topk_kernel<N, false>, grid, block, s, partial, nsplit, T, E, bias, G, TG,   \
-                       K, norm, scale, topk_idx, topk_w, bitmap, words, counts, fd)
+#define MOE_TOPK(N)                                                                                        \
+  if (fd.done)                                                                                             \
+    launch(tr, router_topk_kernel<N, true>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, norm, scale, \
+           topk_idx, topk_w, bitmap, words, counts, fd);                                                  \
+  else                                                                                                     \
+    launch(tr, router_topk_kernel<N, false>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, norm, scale, \
+           topk_idx, topk_w, bitmap, words, counts, fd)
   switch (epl) {
     case 1: MOE_TOPK(1); break;
     case 2: MOE_TOPK(2); break;

@@ -70,6 +70,7 @@ def test_symbols_map_to_steps():
     assert bench._step("router_topk_kernel<8, true>") == "router_topk"
     assert bench._step("router_logits_kwaves_kernel<4>") == "router_logits"
     assert bench._step("router_logits_kernel<8, 2>") == "router_logits"
+    assert bench._step("dispatch_count_kernel") == "dispatch_count"
     assert bench._step("something_else") is None
 
 
