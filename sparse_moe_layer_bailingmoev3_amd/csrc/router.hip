@@ -66,32 +66,56 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const float* wr[RF];
 #pragma unroll
   for (int f = 0; f < RF; ++f) wr[f] = w + (size_t)(e_base + f * 16 + r16) * H + k0 + q * 8;
-  const uint16_t* xr[MF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    int t = min(m0 + mf * 16 + r16, T - 1);
-    xr[mf] = x + (size_t)t * H + k0 + q * 8;
-  }
   floatx4 acc[RF][MF];
 #pragma unroll
   for (int f = 0; f < RF; ++f)
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) acc[f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kk = 0; kk < kchunk; kk += 32) {
+  // The workgroup's token tile (16*MF rows x 32 k per step) is loaded once, by all threads, and
+  // shared through LDS (each wave used to load all of it itself: two thirds of the loads);
+  // weights go straight to registers.  Loads run D steps ahead in a register ring, issued
+  // unconditionally (steps past the end reload the last one) so the waits stay exact.
+  constexpr int BMX = 16 * MF, LX = 40;  // 80-byte LDS rows: 8 consecutive rows hit distinct banks
+  constexpr int XCH = BMX * 4;           // 16-byte pieces of the tile per step
+  constexpr int XPT = (XCH + 255) / 256;
+  constexpr int D = 3;
+  __shared__ __align__(16) uint16_t xs[2][BMX * LX];
+  const int nsteps = kchunk / 32;
+  const uint16_t* xsrc[XPT];
+  int xdst[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c < XCH ? c >> 2 : 0, col = (c & 3) * 8;
+    xsrc[i] = x + (size_t)min(m0 + row, T - 1) * H + k0 + col;
+    xdst[i] = c < XCH ? row * LX + col : -1;
+  }
+  struct Stage {
+    u32x4 xv[XPT];
     float4 a[RF][2];
+  };
+  auto load = [&](Stage& st, int step) {
+    const int kk = min(step, nsteps - 1) * 32;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) st.xv[i] = *(const u32x4*)(xsrc[i] + kk);
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
-      a[f][0] = *(const float4*)(wr[f] + kk);
-      a[f][1] = *(const float4*)(wr[f] + kk + 4);
+      st.a[f][0] = *(const float4*)(wr[f] + kk);
+      st.a[f][1] = *(const float4*)(wr[f] + kk + 4);
     }
-    u32x4 xv[MF];
+  };
+  auto store_x = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) xv[mf] = *(const u32x4*)(xr[mf] + kk);
+    for (int i = 0; i < XPT; ++i)
+      if (xdst[i] >= 0) *(u32x4*)(xs[buf] + xdst[i]) = st.xv[i];
+  };
+  auto compute = [&](const Stage& st, int buf) {
     u32x4 hi[RF], mid[RF], lo[RF];
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
-      const float v[8] = {a[f][0].x, a[f][0].y, a[f][0].z, a[f][0].w, a[f][1].x, a[f][1].y, a[f][1].z, a[f][1].w};
+      const float v[8] = {st.a[f][0].x, st.a[f][0].y, st.a[f][0].z, st.a[f][0].w,
+                          st.a[f][1].x, st.a[f][1].y, st.a[f][1].z, st.a[f][1].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t h, m, l;
@@ -102,13 +126,32 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       }
     }
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+    for (int mf = 0; mf < MF; ++mf) {
+      const u32x4 xv = *(const u32x4*)(xs[buf] + (mf * 16 + r16) * LX + q * 8);
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
-        acc[f][mf] = mfma16(lo[f], xv[mf], acc[f][mf]);
-        acc[f][mf] = mfma16(mid[f], xv[mf], acc[f][mf]);
-        acc[f][mf] = mfma16(hi[f], xv[mf], acc[f][mf]);
+        acc[f][mf] = mfma16(lo[f], xv, acc[f][mf]);
+        acc[f][mf] = mfma16(mid[f], xv, acc[f][mf]);
+        acc[f][mf] = mfma16(hi[f], xv, acc[f][mf]);
       }
+    }
+  };
+  Stage ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) load(ring[j], j);
+  store_x(ring[0], 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int st = s0 + j;
+      if (st < nsteps) {
+        compute(ring[j], st & 1);
+        store_x(ring[(j + 1) % D], (st + 1) & 1);
+      }
+      load(ring[j], st + D);
+      __syncthreads();
+    }
   }
   // result: lane holds token r16 of each fragment, experts 4q .. 4q+3 of each 16-row block
   float* out = partial + (size_t)split * T * E;
