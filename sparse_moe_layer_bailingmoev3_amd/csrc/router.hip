@@ -495,8 +495,9 @@ RouterPlan router_plan(int64_t T, int H, int E) {
   RouterPlan p;
   p.mf = pick_router_mf(T);
   p.m_tiles = (int)((T + 16 * p.mf - 1) / (16 * p.mf));
-  // large T: 128 experts per workgroup (x re-read E/128 times); small T: 64 for more blocks
-  p.rf = (E % 128 == 0 && p.m_tiles >= 32) ? 2 : 1;
+  // 128 experts per workgroup (x re-read E/128 times) once that still gives ~512 workgroups,
+  // else 64 (measured: 512 workgroups of 64 experts at T = 8192, 512 of 128 at T = 16384)
+  p.rf = (E % 128 == 0 && (int64_t)p.m_tiles * (E / 128) >= 512) ? 2 : 1;
   p.n_tiles = E / (64 * p.rf);
   // split the hidden dimension while there are fewer than ~256 workgroups (the chip has
   // 256 CUs); each split is a multiple of 32 that divides H, and at most 10 splits keep
