@@ -88,7 +88,7 @@ struct TStage {
 // One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
 // tile) are issued while step s computes, all in one batch, so that waiting for the token
 // tile of the next step (loads complete in issue order) never waits for younger weights.
-template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4>
+template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4, bool PADDED>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nrows, int rb0, int nrb_here,
                                          uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
@@ -101,9 +101,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
   constexpr int ROWS = NW * RF * 16;
   constexpr int WREGS = FP4 ? 1 : SUB;
-  // loop form (each measured fastest for its kernels): tiles of 64+ tokens and the MXFP4
-  // kernel (128-value steps) issue every load unconditionally; 16- and 32-token tiles do not
-  constexpr bool PADDED = KS == 128 || MF >= 4;
+  // PADDED, the loop form (each measured fastest for its kernels): tiles of 64+ tokens and
+  // the MXFP4 kernel issue every load unconditionally; 16- and 32-token tiles do not
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -331,9 +330,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   }
 }
 
-template <int NW, int RF, int MF, int D, int MODE, int FMT>
+template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS>
 __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
-  constexpr int KS = FMT == FMT_MXFP4 ? 128 : 64;
+  constexpr bool PADDED = FMT == FMT_MXFP4 || MF >= 4;
   constexpr int BM = MF * 16;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
   __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 16)];
@@ -363,11 +362,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int nrows = min(BM, cnt - m0);
   if constexpr (FMT == FMT_MXFP4) {
     if (e < a.E) {
-      ffn_tile<NW, RF, MF, D, MODE, KS, true>(a, e, m0, nrows, rb0, nrb_here, lds);
+      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, m0, nrows, rb0, nrb_here, lds);
       return;
     }
   }
-  ffn_tile<NW, RF, MF, D, MODE, KS, false>(a, e, m0, nrows, rb0, nrb_here, lds);
+  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, m0, nrows, rb0, nrb_here, lds);
 }
 
 // single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan
@@ -394,18 +393,25 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 
 // Kernel configuration per (tile size, weight format, GEMM): NW waves, RF 16-row weight
 // blocks per wave (rows per workgroup and matrix NW*RF*16: 128, or 64 for decode gate/up,
-// whose smaller workgroups measured 4 % faster), D steps of loads in flight.  The down GEMM
-// reads two h planes per token fragment, so it keeps two weight blocks per wave to halve
-// its LDS reads per MFMA.
+// whose smaller workgroups measured 4 % faster), KS values of k per step, D steps of loads in
+// flight.  The down GEMM reads two h planes per token fragment, so it keeps two weight blocks
+// per wave to halve its LDS reads per MFMA.  16-token bf16 tiles (decode) take 256-value
+// steps, two in flight: each weight row then goes out in 512-byte runs (measured: decode
+// gate/up 311 -> 297 us, down 161 -> 159 us against 64-value steps); where K is not a
+// multiple of 256 they fall back to 128-value steps, four in flight (KS_ALT, D_ALT).
 template <int MF, int FMT, int MODE> struct FfnCfg {
   static constexpr bool FP4 = FMT == FMT_MXFP4;
   static constexpr bool DOWN = MODE == MODE_DOWN;
+  static constexpr bool WIDE = MF == 1 && !FP4;
   static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
   static constexpr int RF = (MF == 1 && !DOWN && !FP4) ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
-  static constexpr int D = MF <= 2 ? (FP4 ? 3 : 4)
+  static constexpr int KS = FP4 ? 128 : WIDE ? 256 : 64;
+  static constexpr int D = WIDE ? 2
+                         : MF <= 2 ? (FP4 ? 3 : 4)
                          : MF == 4 ? (FP4 ? 2 : 4)
                          : MF == 8 ? (FP4 ? 2 : (DOWN ? 3 : 4))
                                    : 2;
+  static constexpr int KS_ALT = WIDE ? 128 : KS, D_ALT = WIDE ? 4 : D;
 };
 
 template <int MF, int MODE, int FMT>
@@ -419,7 +425,13 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   int64_t work = max_tiles * (a.bm_list / (16 * MF)) * a.ngroups;
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
+  if (a.K % C::KS == 0)
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
+  else if (C::KS_ALT != C::KS && a.K % C::KS_ALT == 0)
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT>, dim3((unsigned)grid), dim3(C::NW * 64), s,
+           a);
+  else
+    return hipErrorInvalidValue;
   hipError_t err = hipGetLastError();
   if (tr) tr->mark(MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
   return err;
