@@ -392,10 +392,11 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 }
 
 // Kernel configuration per (tile size, weight format, GEMM): NW waves, RF 16-row weight
-// blocks per wave (rows per workgroup and matrix NW*RF*16: 128, or 64 for decode gate/up,
-// whose smaller workgroups measured 4 % faster), KS values of k per step, D steps of loads in
-// flight.  The down GEMM reads two h planes per token fragment, so it keeps two weight blocks
-// per wave to halve its LDS reads per MFMA.  16-token bf16 tiles (decode) take 256-value
+// blocks per wave (rows per workgroup and matrix NW*RF*16: 128, or 64 for the 16-token bf16
+// tiles of decode, whose smaller workgroups measured faster: gate/up 4 %, down 1.5 %), KS
+// values of k per step, D steps of loads in flight.  Otherwise the down GEMM, which reads two
+// h planes per token fragment, keeps two weight blocks per wave to halve its LDS reads per
+// MFMA.  16-token bf16 tiles (decode) take 256-value
 // steps, two in flight: each weight row then goes out in 512-byte runs (measured: decode
 // gate/up 311 -> 297 us, down 161 -> 159 us against 64-value steps); where K is not a
 // multiple of 256 they fall back to 128-value steps, four in flight (KS_ALT, D_ALT).
@@ -404,7 +405,7 @@ template <int MF, int FMT, int MODE> struct FfnCfg {
   static constexpr bool DOWN = MODE == MODE_DOWN;
   static constexpr bool WIDE = MF == 1 && !FP4;
   static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
-  static constexpr int RF = (MF == 1 && !DOWN && !FP4) ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
+  static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
   static constexpr int KS = FP4 ? 128 : WIDE ? 256 : 64;
   static constexpr int D = WIDE ? 2
                          : MF <= 2 ? (FP4 ? 3 : 4)
@@ -475,7 +476,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
   p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
-  p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one 128-row block per workgroup (measured)
+  p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one row block per workgroup (measured)
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
   return p;
