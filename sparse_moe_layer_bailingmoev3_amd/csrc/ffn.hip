@@ -213,7 +213,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
         }
       }
   };
-  auto compute = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
+  auto compute_at_use = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
     const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
@@ -240,6 +240,53 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
             for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[m][f], tf, acc[m][f][mf]);
         }
       }
+    }
+  };
+  // The token fragments of sub-step s + 1 are read from LDS while sub-step s runs its MFMAs
+  // (scheduling barriers keep the compiler from sinking each read to its first use, which
+  // left every pair of MFMAs waiting on an LDS round trip).  256-token tiles, which have no
+  // registers to spare, read each fragment where it is used.
+  auto compute = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
+    if constexpr (MF > 8) {
+      compute_at_use(st, buf);
+      return;
+    }
+    const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
+    u32x4 tf[2][NTP][MF];
+    auto read_frags = [&](u32x4 (&t)[NTP][MF], int s) {
+      const int col = FP4 ? q * 32 + s * 8 : s * 32 + q * 8;
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int p = 0; p < NTP; ++p) t[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
+    };
+    read_frags(tf[0], 0);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      if (s + 1 < SUB) read_frags(tf[(s + 1) & 1], s + 1);
+      u32x4 wf[NMAT][RF];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          if constexpr (FP4) {
+            wf[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+          } else {
+            wf[m][f] = st.w[m][f][s];
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+#pragma unroll
+        for (int p = NTP - 1; p >= 0; --p) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[m][f], tf[s & 1][p][mf], acc[m][f][mf]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
