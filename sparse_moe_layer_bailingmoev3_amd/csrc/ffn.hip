@@ -260,22 +260,27 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
 #pragma unroll
         for (int p = 0; p < NTP; ++p) t[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
     };
-    read_frags(tf[0], 0);
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      if (s + 1 < SUB) read_frags(tf[(s + 1) & 1], s + 1);
-      u32x4 wf[NMAT][RF];
+    // MXFP4: the weights of sub-step s + 1 are also decoded while sub-step s multiplies
+    u32x4 wf[2][NMAT][RF];
+    auto weights = [&](u32x4 (&w)[NMAT][RF], int s) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
           if constexpr (FP4) {
-            wf[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+            w[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
           } else {
-            wf[m][f] = st.w[m][f][s];
+            w[m][f] = st.w[m][f][s];
           }
         }
+    };
+    read_frags(tf[0], 0);
+    weights(wf[0], 0);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      if (s + 1 < SUB) read_frags(tf[(s + 1) & 1], s + 1);
       __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < SUB) weights(wf[(s + 1) & 1], s + 1);
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
@@ -283,7 +288,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[m][f], tf[s & 1][p][mf], acc[m][f][mf]);
+            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[s & 1][m][f], tf[s & 1][p][mf], acc[m][f][mf]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
