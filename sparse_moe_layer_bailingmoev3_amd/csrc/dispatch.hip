@@ -144,15 +144,35 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
     if (lane >= m) incl += o;
   }
   int pos = base + incl - c;
+  // the set bits in token order, 4 tokens at a time: their slot rows (8 slots per batch,
+  // clamped loads) go out in one batch, and every slot that lists e gets the position
+  constexpr int TB = 4, KB = 8;
   while (bits) {
-    const int bit = __ffs(bits) - 1;
-    bits &= bits - 1;
-    const int t = w * 32 + bit;
-    sorted_token[pos] = t;
-    const int32_t* ti = topk_idx + (size_t)t * K;
-    for (int k = 0; k < K; ++k)
-      if (ti[k] == e) inv_perm[(size_t)t * K + k] = pos;
-    ++pos;
+    int tt[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      tt[i] = -1;
+      if (bits) {
+        tt[i] = w * 32 + __ffs(bits) - 1;
+        bits &= bits - 1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (tt[i] >= 0) sorted_token[pos + i] = tt[i];
+    for (int k0 = 0; k0 < K; k0 += KB) {
+      int v[TB][KB];
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int u = 0; u < KB; ++u) v[i][u] = topk_idx[(size_t)(tt[i] >= 0 ? tt[i] : tt[0]) * K + min(k0 + u, K - 1)];
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+          if (tt[i] >= 0 && k0 + u < K && v[i][u] == e) inv_perm[(size_t)tt[i] * K + k0 + u] = pos + i;
+    }
+    pos += TB;
   }
   if (chunk == nchunks - 1) {
     // a token listing the same expert twice is counted twice but has one bit: mark the
