@@ -151,8 +151,9 @@ moe::FfnWeights ffn_weights(const moe_config_t* c, const moe_expert_weights_t* w
 
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
-// mark: also clear (logits kernel) and fill (top-k kernel) the dispatch bitmap and the
-// expert histogram in the workspace, so moe_dispatch's clear and mark kernels are not needed
+// mark: also clear (logits kernel) the dispatch bitmap and histogram in the workspace and fill
+// the bitmap (top-k kernel), so moe_dispatch's clear and mark kernels are not needed (the
+// dispatch counts the histogram from the bitmap)
 // fd (optional, with mark): finish the dispatch inside the top-k kernel; its counter is the
 // histogram's spare last entry
 moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const float* rw, const float* bias,
@@ -170,10 +171,9 @@ moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const flo
   hipError_t e = moe::launch_router_logits(p, (const uint16_t*)x, rw, (int)T, c->hidden_size, c->num_experts,
                                            partial, bitmap, clear_words, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router logits launch");
-  // the histogram is counted from the bitmap by the dispatch (no histogram atomics here)
   e = moe::launch_router_topk(partial, p.nsplit, (int)T, c->num_experts, bias, c->n_group, c->topk_group,
                               c->num_experts_per_tok, c->norm_topk_prob, c->routed_scaling_factor, idx, wts, bitmap,
-                              nullptr, fd ? *fd : none, s, tr);
+                              fd ? *fd : none, s, tr);
   if (e != hipSuccess) return hip_fail(e, "router top-k launch");
   return MOE_OK;
 }

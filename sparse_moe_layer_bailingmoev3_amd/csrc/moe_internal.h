@@ -76,8 +76,7 @@ constexpr int FUSED_DISPATCH_MAX_PAIRS = 4096;  // tokens x slots
 constexpr int FUSED_DISPATCH_MAX_E = 1024;
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G,
                               int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
-                              uint32_t* bitmap, int32_t* counts, const FusedDispatch& fd, hipStream_t s,
-                              Tracer* tr = nullptr);
+                              uint32_t* bitmap, const FusedDispatch& fd, hipStream_t s, Tracer* tr = nullptr);
 
 // ---- dispatch ----------------------------------------------------------------
 size_t dispatch_bitmap_words(int64_t T, int E);

@@ -268,8 +268,7 @@ template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ partial, int nsplit, int T, int E,
                                             const float* __restrict__ bias, int G, int TG, int K, int norm,
                                             float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                            uint32_t* __restrict__ bitmap, int words, int32_t* __restrict__ counts,
-                                            int t, int lane) {
+                                            uint32_t* __restrict__ bitmap, int words, int t, int lane) {
   const int e0 = lane * EPL;
 
   // logits: split partial sums added in split order
@@ -350,11 +349,10 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
     topk_w[(size_t)t * K + pos] = wv;
     if (bitmap) {
       // dispatch: one bit per (expert, token) (an integer atomic, so the final bitmap does
-      // not depend on the order); the histogram is added here only if asked for; otherwise
-      // it is the popcount of the bitmap rows (one atomic per pair on 512 counters
-      // serialises: 30 us of the top-k kernel at 8192 tokens, 100 us on skewed routing)
+      // not depend on the order).  The histogram is the popcount of the bitmap rows, taken
+      // later: one atomic per pair on 512 counters serialised on the hot ones (30 us of this
+      // kernel at 8192 tokens, 100 us on skewed routing).
       atomicOr(&bitmap[(size_t)my_idx * words + (t >> 5)], 1u << (t & 31));
-      if (counts) atomicAdd(&counts[my_idx], 1);
     }
   }
 }
@@ -477,12 +475,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w,
                                                           uint32_t* __restrict__ bitmap, int words,
-                                                          int32_t* __restrict__ counts, FusedDispatch fd) {
+                                                          FusedDispatch fd) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   // the fused dispatch builds its bitmap and histogram from topk_idx itself
   if (t < T) route_token<EPL>(partial, nsplit, T, E, bias, G, TG, K, norm, scale, topk_idx, topk_w,
-                              FUSED ? nullptr : bitmap, words, counts, t, lane);
+                              FUSED ? nullptr : bitmap, words, t, lane);
   if constexpr (FUSED) fused_dispatch_finish(fd, topk_idx, T, K, E);
 }
 
@@ -579,7 +577,7 @@ hipError_t launch_router_logits(const RouterPlan& p, const uint16_t* x, const fl
 
 hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, const float* bias, int G, int TG,
                               int K, int norm, float scale, int32_t* topk_idx, float* topk_w, uint32_t* bitmap,
-                              int32_t* counts, const FusedDispatch& fd, hipStream_t s, Tracer* tr) {
+                              const FusedDispatch& fd, hipStream_t s, Tracer* tr) {
   if (fd.done && (T > FUSED_DISPATCH_MAX_T || (int64_t)T * K > FUSED_DISPATCH_MAX_PAIRS || E > FUSED_DISPATCH_MAX_E))
     return hipErrorInvalidValue;
   const int words = (T + 31) / 32;
@@ -588,10 +586,10 @@ hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, co
 #define MOE_TOPK(N)                                                                                        \
   if (fd.done)                                                                                             \
     launch(tr, router_topk_kernel<N, true>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, norm, scale, \
-           topk_idx, topk_w, bitmap, words, counts, fd);                                                  \
+           topk_idx, topk_w, bitmap, words, fd);                                                          \
   else                                                                                                     \
     launch(tr, router_topk_kernel<N, false>, grid, block, s, partial, nsplit, T, E, bias, G, TG, K, norm, scale, \
-           topk_idx, topk_w, bitmap, words, counts, fd)
+           topk_idx, topk_w, bitmap, words, fd)
   switch (epl) {
     case 1: MOE_TOPK(1); break;
     case 2: MOE_TOPK(2); break;
