@@ -190,6 +190,30 @@ def measure(shape, d, steps, warmup, hip):
     return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, dom=dom, dom_ms=dom_ms, counts=counts, out=out)
 
 
+def time_bias_update(shape, counts, hip, reps=200):
+    """Mean duration of the expert-bias update (one workgroup) on the counts of a real step:
+    reps back-to-back launches between two events.  Bytes it must move: E counts read, E
+    biases read and written (12 bytes per expert); it is a single-workgroup, latency-bound
+    kernel, so its figure is a duration, not a bandwidth."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    cfg = cfg_for(shape)
+    cnt = torch.from_numpy(np.ascontiguousarray(counts[:shape.E + 1]).astype(np.int32)).cuda()
+    bias = torch.zeros(shape.E, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(5):
+        moe.moe_update_expert_bias(cfg, cnt, bias, 1e-3)
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for _ in range(reps):
+        moe.moe_update_expert_bias(cfg, cnt, bias, 1e-3)
+    hip.record(b, stream)
+    us = hip.elapsed_ms(a, b) * 1e3 / reps
+    return {"us_per_call": round(us, 2), "bytes": 12 * shape.E, "calls": reps,
+            "note": "sign-rule expert-bias update from the step's counts; one workgroup, latency-bound"}
+
+
 def roofline(shape, r, workload=None):
     """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
     bound to its dispatch in every step of the timed region.
@@ -453,6 +477,7 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in r["kernels"].items()},
         "kernels_ms_from": "forwards with an event after every kernel, outside the timed region",
         "event_ms_per_step": round(r["event_ms"], 4),
+        "expert_bias_update": time_bias_update(shape, r["counts"], hip),
     }
     if not args.no_prefill and shape.name == "decode":
         p = CONFIGS["prefill"]

@@ -158,6 +158,22 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
                          int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Expert-bias update, the step after the layer in training (routing walk-through page,
+ * section 三.3: every routed expert's selection bias is lowered when it is busy and raised
+ * when it is idle, balancing the load without an auxiliary loss).  The page gives neither the
+ * rule nor the rate; this library takes the sign rule with a caller-chosen step gamma:
+ *   bias[e] += gamma   if counts[e] * E < sum(counts)   (below the mean count)
+ *   bias[e] -= gamma   if counts[e] * E > sum(counts)   (above it; unchanged at the mean)
+ * computed as bias[e] + gamma * (+1 | -1 | 0) in fp32, the decision taken in integers.
+ *   expert_counts  device int32 [E]: the routed counts of a step (the first E entries of the
+ *                  expert_counts of moe_dispatch or moe_forward; the shared expert's is not read)
+ *   expert_bias    device fp32 [E], updated in place (the array moe_route/moe_forward read)
+ *   gamma          the step; any finite value (MOE_ERR_INVALID_ARG otherwise)
+ * Enqueued on `stream`; it reads the counts when it runs, so it may follow the forward that
+ * writes them on the same stream without a host synchronisation. */
+moe_status_t moe_update_expert_bias(const moe_config_t* cfg, const int32_t* expert_counts,
+                                    float* expert_bias, float gamma, void* stream);
+
 /* moe_forward with a timing trace, for profiling (same results).  events[0] is recorded on
  * `stream` before the first kernel and events[i+1] right after the i-th kernel launch; the
  * caller creates the events (hipEvent_t, passed as void*) and later reads the elapsed times;

@@ -5,4 +5,5 @@ benchmark's CPU-baseline leg.  The HIP library never calls it and shares no code
 with it.
 """
 from .moe_oracle import (Dispatch, Routing, bf16_to_f64, dispatch, expert_forward,  # noqa: F401
-                         expert_hidden, moe_layer, mxfp4_dequant, route, router_logits, swiglu)
+                         expert_hidden, moe_layer, mxfp4_dequant, route, router_logits, swiglu,
+                         update_expert_bias)

@@ -229,3 +229,26 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray],
     if shared is not None:
         out += expert_forward(x, *shared, shared_swiglu_limit)
     return out, r
+
+
+# ----------------------------------------------------------------------------------
+# expert-bias update (the step after the layer in training)
+# ----------------------------------------------------------------------------------
+def update_expert_bias(bias: np.ndarray, counts: np.ndarray, gamma: float) -> np.ndarray:
+    """[R] section 三.3: every routed expert carries a selection bias that is lowered for
+    experts that receive many tokens and raised for those that receive few, so that the load
+    evens out without an auxiliary loss.  The page gives neither the rule nor the rate; the
+    reading taken here is the sign rule with a fixed step gamma: an expert above the mean
+    count moves down by gamma, one below it moves up by gamma, one exactly at the mean stays.
+    "Above the mean" is decided in integers (count_e * E against the total of the E counts),
+    so no rounding enters the decision; the bias is router state, kept in fp32 ([R] section
+    四), so the new value is the fp32 sum bias + (+-gamma).
+
+    bias: [E] fp32; counts: the E routed counts (a longer array, such as the [E+1] counts
+    with the shared expert last, is cut to E)."""
+    b = np.asarray(bias, dtype=np.float32)
+    E = b.shape[0]
+    c = np.asarray(counts, dtype=np.int64)[:E]
+    side = np.sign(c.sum() - E * c)  # +1 below the mean, -1 above, 0 at the mean
+    step = np.float32(gamma) * side.astype(np.float32)
+    return (b + step).astype(np.float32)

@@ -17,14 +17,15 @@ from typing import Optional
 
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
-           "moe_forward_timed", "moe_status_string",
+           "moe_forward_timed", "moe_update_expert_bias", "moe_status_string",
            "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "EXPORTED_SYMBOLS"]
 
 MOE_WEIGHTS_BF16 = 0
 MOE_WEIGHTS_MXFP4 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                    "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_status_string", "moe_last_error")
+                    "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_update_expert_bias",
+                    "moe_status_string", "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -88,6 +89,7 @@ def load_library():
         "moe_forward_traced": [C, I64, P, P, P, W, P, P, SZ, P, ctypes.POINTER(P), ctypes.c_int32,
                                ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int32)],
         "moe_forward_timed": [C, I64, P, P, P, W, P, P, SZ, P, ctypes.c_int32, P, P],
+        "moe_update_expert_bias": [C, P, P, ctypes.c_float, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -192,3 +194,9 @@ def moe_forward_timed(cfg, T, x, router_w, expert_bias, weights: MoEExpertWeight
     _check(load_library().moe_forward_timed(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
                                             ctypes.byref(weights.struct), _ptr(out), p, n, _stream(stream),
                                             kernel_index, start_event, stop_event))
+
+
+def moe_update_expert_bias(cfg, expert_counts, expert_bias, gamma, stream=None):
+    """In-place sign-rule update of the routed experts' selection bias from a step's counts."""
+    _check(load_library().moe_update_expert_bias(ctypes.byref(cfg), _ptr(expert_counts), _ptr(expert_bias),
+                                                 float(gamma), _stream(stream)))

@@ -297,6 +297,20 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x, c
   return do_ffn(cfg, T, x, expert_offsets, sorted_token, weights, y_sorted, L, ws, (hipStream_t)stream);
 }
 
+moe_status_t moe_update_expert_bias(const moe_config_t* cfg, const int32_t* expert_counts, float* expert_bias,
+                                    float gamma, void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, 0);
+  if (st != MOE_OK) return st;
+  MOE_CHECK_PTR(expert_counts, "expert_counts");
+  MOE_CHECK_PTR(expert_bias, "expert_bias");
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
+  hipError_t e = moe::launch_expert_bias_update(expert_counts, cfg->num_experts, gamma, expert_bias,
+                                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "expert bias update launch");
+  return MOE_OK;
+}
+
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_sorted, const int32_t* inv_perm,
                          const float* topk_w, void* out, void* stream) {
   g_last_error.clear();

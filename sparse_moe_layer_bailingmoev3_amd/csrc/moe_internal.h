@@ -78,6 +78,9 @@ hipError_t launch_router_topk(const float* partial, int nsplit, int T, int E, co
                               int TG, int K, int norm, float scale, int32_t* topk_idx, float* topk_w,
                               uint32_t* bitmap, const FusedDispatch& fd, hipStream_t s, Tracer* tr = nullptr);
 
+// expert-bias update from the routed counts (one workgroup; E <= 1024)
+hipError_t launch_expert_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s);
+
 // ---- dispatch ----------------------------------------------------------------
 size_t dispatch_bitmap_words(int64_t T, int E);
 // marked: the bitmap was already filled by the router's top-k kernel (and cleared by its

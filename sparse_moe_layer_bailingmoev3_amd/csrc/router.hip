@@ -487,7 +487,36 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 int pick_router_mf(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8; }
 
+// Expert-bias update (routing walk-through page, section 三.3: the selection bias of a busy
+// expert is lowered and that of an idle one raised, with no auxiliary loss; the page gives no
+// rule or rate, the sign rule is taken): one workgroup; the total count is summed in 64 bits
+// and each expert compares count * E with it, so the decision involves no rounding.
+__global__ __launch_bounds__(1024) void expert_bias_update_kernel(const int32_t* __restrict__ counts, int E,
+                                                                  float gamma, float* __restrict__ bias) {
+  __shared__ long long wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  const long long c = e < E ? (long long)counts[e] : 0;
+  long long v = c;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total += wsum[w];
+  if (e < E) {
+    const long long d = total - (long long)E * c;  // > 0: below the mean
+    const float side = d > 0 ? 1.0f : d < 0 ? -1.0f : 0.0f;
+    bias[e] = bias[e] + gamma * side;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_expert_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s) {
+  if (E <= 0 || E > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_bias_update_kernel, dim3(1), dim3((E + 63) / 64 * 64), 0, s, counts, E, gamma, bias);
+  return hipGetLastError();
+}
 
 RouterPlan router_plan(int64_t T, int H, int E) {
   RouterPlan p;

@@ -122,6 +122,23 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
     assert b"scale" in lib.moe_last_error()
 
 
+def test_bias_update_rejects_bad_arguments_before_any_launch():
+    cfg = cfg_for(CONFIGS["decode"])
+    lib = moe.load_library()
+    fake = 1 << 40
+    assert lib.moe_update_expert_bias(ctypes.byref(cfg), None, fake, 1e-3, None) == -1
+    assert b"expert_counts" in lib.moe_last_error()
+    assert lib.moe_update_expert_bias(ctypes.byref(cfg), fake, None, 1e-3, None) == -1
+    assert b"expert_bias" in lib.moe_last_error()
+    for g in (float("nan"), float("inf"), -float("inf")):
+        assert lib.moe_update_expert_bias(ctypes.byref(cfg), fake, fake, g, None) == -1
+        assert b"gamma" in lib.moe_last_error()
+    assert lib.moe_update_expert_bias(None, fake, fake, 1e-3, None) == -1
+    bad = cfg_for(CONFIGS["decode"])
+    bad.num_experts = 500
+    assert lib.moe_update_expert_bias(ctypes.byref(bad), fake, fake, 1e-3, None) == -2
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = cfg_for(CONFIGS["decode"])
     lib = moe.load_library()

@@ -244,6 +244,46 @@ def test_traced_and_timed_forwards_match_forward(T):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_expert_bias_update_matches_oracle(name):
+    """The bias update from a forward's own counts, on the same stream, bit for bit against
+    the oracle (routing walk-through page, section 三.3, sign rule); then a balanced
+    histogram, which must leave the bias as it is."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    s = CONFIGS[name]
+    c = host_case(s, seed=12, T=64) if name == "tiny" else None
+    if c is None:
+        cfg = moe.MoEConfig(hidden_size=s.H, num_experts=s.E, num_experts_per_tok=s.K, n_group=s.G,
+                            topk_group=s.TG, moe_intermediate_size=s.I, num_shared_experts=1,
+                            shared_intermediate_size=s.I_s, norm_topk_prob=1, routed_scaling_factor=2.5,
+                            swiglu_limit=0.0, shared_swiglu_limit=0.0, expert_weight_format=moe.MOE_WEIGHTS_BF16)
+        rng = np.random.default_rng(12)
+        counts_h = rng.poisson(1.0, size=s.E + 1).astype(np.int32)
+        counts = torch.from_numpy(counts_h).cuda()
+    else:
+        dev = DeviceCase(c)
+        cfg = dev.cfg
+        counts = dev.forward()[3]
+        counts_h = counts.cpu().numpy()
+    say(f"[gpu] moe_update_expert_bias {name} E={s.E}")
+    rng = np.random.default_rng(13)
+    bias_h = rng.uniform(-0.1, 0.1, size=s.E).astype(np.float32)
+    bias_h[:3] = [0.0, -0.0, 1.0]
+    bias = torch.from_numpy(bias_h.copy()).cuda()
+    gamma = 1e-3
+    moe.moe_update_expert_bias(cfg, counts, bias, gamma)
+    torch.cuda.synchronize()
+    want = oracle.update_expert_bias(bias_h, counts_h, gamma)
+    got = bias.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a second step from a balanced histogram changes nothing
+    flat = torch.full((s.E + 1,), 5, dtype=torch.int32, device="cuda")
+    moe.moe_update_expert_bias(cfg, flat, bias, gamma)
+    torch.cuda.synchronize()
+    assert np.array_equal(bias.cpu().numpy().view(np.uint32), oracle.update_expert_bias(want, np.full(s.E + 1, 5), gamma).view(np.uint32))
+
+
 # ----------------------------------------------------------------------------------
 # adversarial fixtures (tiny layer)
 # ----------------------------------------------------------------------------------
