@@ -214,6 +214,38 @@ def time_bias_update(shape, counts, hip, reps=200):
             "note": "sign-rule expert-bias update from the step's counts; one workgroup, latency-bound"}
 
 
+def measure_dense(T, H, I, steps, warmup, hip):
+    """The dense SwiGLU FFN (moe_dense_ffn) at T tokens: seeded bf16 inputs, `steps` timed calls
+    between two events.  Algorithmic bytes: the three weight matrices once (3*I*H*2) + x read
+    + out written; flops 6*T*H*I."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    wg, wu = (torch.randn((I, H), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16) for _ in range(2))
+    wd = torch.randn((H, I), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_dense_ffn_workspace_size(H, I, T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        moe.moe_dense_ffn(H, I, 0.0, T, x, wg, wu, wd, out, ws)
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for _ in range(steps):
+        moe.moe_dense_ffn(H, I, 0.0, T, x, wg, wu, wd, out, ws)
+    hip.record(b, stream)
+    ms = hip.elapsed_ms(a, b) / steps
+    byts = 3 * I * H * 2 + 2 * T * H * 2
+    flops = 6.0 * T * H * I
+    hbm, mfma = byts / (ms * 1e-3) / 1e9, flops / (ms * 1e-3) / 1e12
+    bound = "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    frac = hbm / HBM_PEAK_GBS if bound == "hbm" else mfma / BF16_PEAK_TFLOPS
+    return {"workload": f"dense SwiGLU FFN: T={T}, hidden {H}, intermediate {I}", "value": round(T / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_call": round(ms, 4), "bound": bound, "frac": round(frac, 4),
+            "hbm_GBps": round(hbm, 1), "bf16_TFLOPs": round(mfma, 1), "algorithmic_bytes": byts, "flops": flops}
+
+
 def roofline(shape, r, workload=None):
     """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
     bound to its dispatch in every step of the timed region.
@@ -421,6 +453,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
+    ap.add_argument("--dense", type=int, default=0, metavar="I",
+                    help="instead: the dense SwiGLU FFN (moe_dense_ffn) of intermediate size I at T=1, 64, 512, 8192")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ from the rocprofv3 runs in DIR and exit")
@@ -437,6 +471,13 @@ def main():
     from synthetic import CONFIGS, gen_experts
     import sparse_moe_layer_bailingmoev3_amd as moe
     moe.load_library()  # no fallback: fails loudly without the HIP library
+    if args.dense:
+        hip = Hip()
+        H = CONFIGS["decode"].H
+        res = [measure_dense(T, H, args.dense, max(args.steps, 10), args.warmup, hip) for T in (1, 64, 512, 8192)]
+        print(json.dumps({"metric": "dense SwiGLU FFN tokens/s", "dtype": "bf16", "data": "synthetic (seeded)",
+                          "n_gpus": 1, "results": res}), flush=True)
+        return
     assert torch.cuda.is_available(), "no GPU visible"
     hip = Hip()
 

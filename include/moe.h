@@ -158,6 +158,23 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
                          int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Dense SwiGLU FFN, the layers before the MoE stack (routing walk-through page, section 二:
+ * first_k_dense_replace = 2, the first two of the 42 layers use an ordinary dense FFN; the
+ * page gives no intermediate size, so it is a parameter, and the FFN is read as the experts'
+ * own SwiGLU form):  out[t] = ( silu(x[t] gate^T) * (x[t] up^T) ) down^T, the activation
+ * clamped to +-swiglu_limit when it is > 0, fp32 accumulation, one rounding to bf16.
+ * It runs as a layer with a single routed expert that every token takes with weight 1, on
+ * the same kernels as moe_expert_ffn and moe_combine.
+ *   x device bf16 [T,H]; gate, up device bf16 [I,H]; down device bf16 [H,I]; out device
+ *   bf16 [T,H]; ws device, 256-byte aligned, moe_dense_ffn_workspace_size bytes.
+ *   H and I multiples of 128 (MOE_ERR_UNSUPPORTED otherwise); T = 0 is a no-op.
+ * Results are deterministic. */
+moe_status_t moe_dense_ffn_workspace_size(int32_t hidden_size, int32_t intermediate_size, int64_t T,
+                                          size_t* bytes);
+moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float swiglu_limit, int64_t T,
+                           const void* x, const void* gate, const void* up, const void* down, void* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Expert-bias update, the step after the layer in training (routing walk-through page,
  * section 三.3: every routed expert's selection bias is lowered when it is busy and raised
  * when it is idle, balancing the load without an auxiliary loss).  The page gives neither the

@@ -17,7 +17,8 @@ from typing import Optional
 
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
-           "moe_forward_timed", "moe_update_expert_bias", "moe_status_string",
+           "moe_forward_timed", "moe_update_expert_bias", "moe_dense_ffn_workspace_size", "moe_dense_ffn",
+           "moe_status_string",
            "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "EXPORTED_SYMBOLS"]
 
 MOE_WEIGHTS_BF16 = 0
@@ -25,7 +26,7 @@ MOE_WEIGHTS_MXFP4 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_update_expert_bias",
-                    "moe_status_string", "moe_last_error")
+                    "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_status_string", "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -90,6 +91,8 @@ def load_library():
                                ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int32)],
         "moe_forward_timed": [C, I64, P, P, P, W, P, P, SZ, P, ctypes.c_int32, P, P],
         "moe_update_expert_bias": [C, P, P, ctypes.c_float, P],
+        "moe_dense_ffn_workspace_size": [ctypes.c_int32, ctypes.c_int32, I64, ctypes.POINTER(SZ)],
+        "moe_dense_ffn": [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I64, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -200,3 +203,16 @@ def moe_update_expert_bias(cfg, expert_counts, expert_bias, gamma, stream=None):
     """In-place sign-rule update of the routed experts' selection bias from a step's counts."""
     _check(load_library().moe_update_expert_bias(ctypes.byref(cfg), _ptr(expert_counts), _ptr(expert_bias),
                                                  float(gamma), _stream(stream)))
+
+
+def moe_dense_ffn_workspace_size(hidden_size, intermediate_size, T) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().moe_dense_ffn_workspace_size(hidden_size, intermediate_size, T, ctypes.byref(n)))
+    return n.value
+
+
+def moe_dense_ffn(hidden_size, intermediate_size, swiglu_limit, T, x, gate, up, down, out, ws, stream=None):
+    """Dense SwiGLU FFN out = (silu(x gate^T) * (x up^T)) down^T (bf16 in and out)."""
+    p, n = _ws(ws)
+    _check(load_library().moe_dense_ffn(hidden_size, intermediate_size, float(swiglu_limit), T, _ptr(x), _ptr(gate),
+                                        _ptr(up), _ptr(down), _ptr(out), p, n, _stream(stream)))

@@ -37,6 +37,23 @@ __global__ void dispatch_mark_kernel(const int32_t* __restrict__ topk_idx, int T
   }
 }
 
+// dense FFN as a one-expert layer: every token is routed to expert 0 in slot 0 with weight 1
+__global__ __launch_bounds__(256) void dense_dispatch_kernel(int T, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_token,
+                                                             int32_t* __restrict__ inv_perm, float* __restrict__ topk_w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+    offsets[2] = T;
+  }
+  if (i < T) {
+    sorted_token[i] = i;
+    inv_perm[i] = i;
+    topk_w[i] = 1.0f;
+  }
+}
+
 // marked bitmap (no expert twice for a token): counts[e] = set bits of row e, one wave per row
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __restrict__ bitmap, int words, int E,
                                                              int32_t* __restrict__ counts) {
@@ -187,6 +204,14 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
 
 size_t dispatch_bitmap_words(int64_t T, int E) { return (size_t)E * (size_t)((T + 31) / 32); }
 
+
+hipError_t launch_dense_dispatch(int T, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, float* topk_w,
+                                 hipStream_t s) {
+  if (T <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_dispatch_kernel, dim3((T + 255) / 256), dim3(256), 0, s, T, offsets, sorted_token, inv_perm,
+                     topk_w);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, uint32_t* bitmap, int32_t* counts,
                            int32_t* counts_out, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, bool marked,

@@ -529,6 +529,17 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
   p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
   p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one row block per workgroup (measured)
+  if (E == 1 && S == 0 && avg <= 1024) {
+    // a single expert (the dense FFN) has no experts to spread over the CUs: tiles of at most
+    // T/8 tokens and one row block per workgroup, so that token tiles x row blocks fill the
+    // chip (each tile re-reads the weights, mostly from the Infinity Cache)
+    p.mf = avg <= 128 ? 1 : avg <= 256 ? 2 : avg <= 512 ? 4 : 8;
+    p.mf_gate_up = p.mf;
+    p.mf_down = std::min(p.mf, 4);
+    p.tiles = false;
+    p.bm = 16 * p.mf;
+    p.rbw_gate_up = p.rbw_down = 1;
+  }
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
   return p;

@@ -297,6 +297,83 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x, c
   return do_ffn(cfg, T, x, expert_offsets, sorted_token, weights, y_sorted, L, ws, (hipStream_t)stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// A dense SwiGLU FFN is the layer with one routed expert that every token picks with weight 1
+// and no shared expert: the same FFN kernels and the same combine (which then only rounds y).
+moe_config_t dense_config(int32_t H, int32_t I, float limit) {
+  moe_config_t c{};
+  c.hidden_size = H;
+  c.num_experts = 1;
+  c.num_experts_per_tok = 1;
+  c.n_group = 1;
+  c.topk_group = 1;
+  c.moe_intermediate_size = I;
+  c.num_shared_experts = 0;
+  c.shared_intermediate_size = 0;
+  c.norm_topk_prob = 0;
+  c.routed_scaling_factor = 1.0f;
+  c.swiglu_limit = limit;
+  c.shared_swiglu_limit = 0.0f;
+  c.expert_weight_format = MOE_WEIGHTS_BF16;
+  return c;
+}
+
+moe_status_t validate_dense(int32_t H, int32_t I, float limit, int64_t T) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)T);
+  if (T > (int64_t)((1u << 31) - 1) / 2) return fail(MOE_ERR_UNSUPPORTED, "T = %lld is too large", (long long)T);
+  if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden_size and intermediate_size must be > 0");
+  if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "hidden_size %d is not a multiple of 128", H);
+  if (I % 128) return fail(MOE_ERR_UNSUPPORTED, "intermediate_size %d is not a multiple of 128", I);
+  if (!std::isfinite(limit)) return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_dense_ffn_workspace_size(int32_t hidden_size, int32_t intermediate_size, int64_t T, size_t* bytes) {
+  g_last_error.clear();
+  moe_status_t st = validate_dense(hidden_size, intermediate_size, 0.0f, T);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes must not be NULL");
+  const moe_config_t dc = dense_config(hidden_size, intermediate_size, 0.0f);
+  *bytes = layout(&dc, T).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float swiglu_limit, int64_t T,
+                           const void* x, const void* gate, const void* up, const void* down, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_dense(hidden_size, intermediate_size, swiglu_limit, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(out, "out");
+  const moe_config_t dc = dense_config(hidden_size, intermediate_size, swiglu_limit > 0 ? swiglu_limit : 0.0f);
+  moe_expert_weights_t w{};
+  w.gate = gate;
+  w.up = up;
+  w.down = down;
+  if ((st = check_weights(&dc, &w)) != MOE_OK) return st;
+  Layout L;
+  if ((st = check_ws(&dc, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* offsets = (int32_t*)at(ws, L.offsets);
+  int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
+  int32_t* inv = (int32_t*)at(ws, L.inv_perm);
+  float* wts = (float*)at(ws, L.topk_w);
+  hipError_t e = moe::launch_dense_dispatch((int)T, offsets, sorted_token, inv, wts, s);
+  if (e != hipSuccess) return hip_fail(e, "dense dispatch launch");
+  void* y = at(ws, L.y);
+  if ((st = do_ffn(&dc, T, x, offsets, sorted_token, &w, y, L, ws, s)) != MOE_OK) return st;
+  return do_combine(&dc, T, y, inv, wts, out, s);
+}
+
 moe_status_t moe_update_expert_bias(const moe_config_t* cfg, const int32_t* expert_counts, float* expert_bias,
                                     float gamma, void* stream) {
   g_last_error.clear();

@@ -92,6 +92,10 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int K, int E, int S, 
                            int32_t* counts, int32_t* counts_out, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
                            bool marked, int32_t* tile_prefix, int bm, hipStream_t s, Tracer* tr = nullptr);
 
+// dense FFN as a one-expert layer: offsets {0, T, T}, identity permutation, slot weight 1
+hipError_t launch_dense_dispatch(int T, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, float* topk_w,
+                                 hipStream_t s);
+
 // ---- expert FFN --------------------------------------------------------------
 struct FfnWeights {
   const void* gate; const void* up; const void* down;

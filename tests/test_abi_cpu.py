@@ -139,6 +139,27 @@ def test_bias_update_rejects_bad_arguments_before_any_launch():
     assert lib.moe_update_expert_bias(ctypes.byref(bad), fake, fake, 1e-3, None) == -2
 
 
+def test_dense_ffn_validation_on_the_host():
+    lib = moe.load_library()
+    fake = 1 << 40
+    assert moe.moe_dense_ffn_workspace_size(2560, 6912, 64) > moe.moe_dense_ffn_workspace_size(2560, 6912, 1) > 0
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_dense_ffn_workspace_size(2560, 700, 64)
+    assert ei.value.status == -2
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_dense_ffn_workspace_size(2500, 768, 64)
+    assert ei.value.status == -2
+    need = moe.moe_dense_ffn_workspace_size(512, 256, 64)
+    assert lib.moe_dense_ffn(512, 256, 0.0, 64, None, fake, fake, fake, fake, fake, need, None) == -1
+    assert lib.moe_dense_ffn(512, 256, 0.0, 64, fake, None, fake, fake, fake, fake, need, None) == -1
+    assert lib.moe_dense_ffn(512, 256, 0.0, 64, fake, fake, fake, fake, fake + 8, fake, need, None) == -3
+    assert lib.moe_dense_ffn(512, 256, 0.0, 64, fake, fake, fake, fake, fake, fake, need - 1, None) == -4
+    assert lib.moe_dense_ffn(512, 256, float("nan"), 64, fake, fake, fake, fake, fake, fake, need, None) == -1
+    assert lib.moe_dense_ffn(512, 256, 0.0, -1, fake, fake, fake, fake, fake, fake, need, None) == -1
+    # T = 0 returns before looking at any pointer
+    assert lib.moe_dense_ffn(512, 256, 0.0, 0, None, None, None, None, None, None, 0, None) == 0
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = cfg_for(CONFIGS["decode"])
     lib = moe.load_library()

@@ -284,6 +284,35 @@ def test_expert_bias_update_matches_oracle(name):
     assert np.array_equal(bias.cpu().numpy().view(np.uint32), oracle.update_expert_bias(want, np.full(s.E + 1, 5), gamma).view(np.uint32))
 
 
+@pytest.mark.parametrize("H,I,T,limit", [(512, 384, 1, 0.0), (512, 384, 70, 0.0), (512, 640, 300, 0.002),
+                                         (512, 384, 1500, 0.0), (2560, 6912, 64, 0.0), (2560, 6912, 1100, 0.0)])
+def test_dense_ffn_matches_oracle(H, I, T, limit):
+    """Dense SwiGLU FFN (the layers before the MoE stack) against the oracle's SwiGLU FFN in
+    float64: every output row at small sizes, 64 sampled rows at the full hidden size."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    rng = np.random.default_rng(20 + T)
+    say(f"[gpu] moe_dense_ffn H={H} I={I} T={T} limit={limit}")
+
+    def bf16(shape, scale):
+        v = (rng.standard_normal(shape) * scale).astype(np.float32)
+        return (v.view(np.uint32) >> 16).astype(np.uint16)  # truncation keeps it exactly bf16
+
+    x, g, u, d = bf16((T, H), 1.0), bf16((I, H), 0.02), bf16((I, H), 0.02), bf16((H, I), 0.02)
+    dev = [to_dev(a, bf16=True) for a in (x, g, u, d)]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_dense_ffn_workspace_size(H, I, T), dtype=torch.uint8, device="cuda")
+    moe.moe_dense_ffn(H, I, limit, T, *dev, out, ws)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T * H <= 512 * 1500 else np.sort(rng.choice(T, size=64, replace=False))
+    xf, gf, uf, df = (oracle.bf16_to_f64(a) for a in (x, g, u, d))
+    ref = oracle.expert_forward(xf[rows], gf, uf, df, limit)
+    got = oracle.bf16_to_f64(to_bits(out))[rows]
+    err = np.abs(got - ref).max() / rms(ref)
+    say(f"      max|err| / RMS = {err:.3e} (bar {TOL_BF16})")
+    assert err <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------------
 # adversarial fixtures (tiny layer)
 # ----------------------------------------------------------------------------------
