@@ -448,14 +448,15 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 // tiles of decode, whose smaller workgroups measured faster: gate/up 4 %, down 1.5 %), KS
 // values of k per step, D steps of loads in flight.  Otherwise the down GEMM, which reads two
 // h planes per token fragment, keeps two weight blocks per wave to halve its LDS reads per
-// MFMA.  16-token bf16 tiles (decode) take 256-value
-// steps, two in flight: each weight row then goes out in 512-byte runs (measured: decode
-// gate/up 311 -> 297 us, down 161 -> 159 us against 64-value steps); where K is not a
+// MFMA.  16-token bf16 tiles (decode) take 256-value steps, two in flight, in 64-row
+// workgroups: each weight row then goes out in 512-byte runs (measured: decode gate/up 311 ->
+// 297 us, down 161 -> 159 us against 64-value steps); so does the gate/up of 32-token tiles
+// (T = 1024: 683 -> 655 us; their down GEMM measured slower that way).  Where K is not a
 // multiple of 256 they fall back to 128-value steps, four in flight (KS_ALT, D_ALT).
 template <int MF, int FMT, int MODE> struct FfnCfg {
   static constexpr bool FP4 = FMT == FMT_MXFP4;
   static constexpr bool DOWN = MODE == MODE_DOWN;
-  static constexpr bool WIDE = MF == 1 && !FP4;
+  static constexpr bool WIDE = !FP4 && (MF == 1 || (MF == 2 && !DOWN));
   static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
   static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
   static constexpr int KS = FP4 ? 128 : WIDE ? 256 : 64;
