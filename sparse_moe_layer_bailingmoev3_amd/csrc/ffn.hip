@@ -522,8 +522,10 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : avg <= 48 ? 4 : (avg <= 192 || fmt == FMT_MXFP4) ? 8 : 16;
   p.mf_gate_up = p.mf;
   p.mf_down = std::min(p.mf, 4);
-  // many tokens per expert and bf16 weights: the 256-token tile kernel (ffn_tile.hip)
-  p.tiles = fmt == FMT_BF16 && avg > 48 && ffn_tiles_supported(H, I);
+  // more than 12 tokens per expert and bf16 weights: the 256-token tile kernel (ffn_tile.hip)
+  // (measured against the small tiles: T = 1024 (16 per expert) 1.094 -> 1.074 ms, T = 1536
+  // 1.297 -> 1.215, T = 2048 1.446 -> 1.294, T = 4096 1.89 -> 1.57)
+  p.tiles = fmt == FMT_BF16 && avg > 12 && ffn_tiles_supported(H, I);
   if (p.tiles) p.mf = 16;
   p.bm = 16 * p.mf;
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
