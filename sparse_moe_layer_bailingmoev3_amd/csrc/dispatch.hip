@@ -115,14 +115,17 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
       }
     }
     int run = incl - sum, trun = tincl - tsum;
+    int4* info = tile_prefix ? (int4*)(tile_prefix + tile_info_offset(E)) : nullptr;
     for (int i = b; i < en; ++i) {
+      const int c = counts[i];
       offsets[i] = run;
-      counts_out[i] = counts[i];
-      run += counts[i];
+      counts_out[i] = c;
       if (tile_prefix) {
         tile_prefix[i] = trun;
-        trun += (counts[i] + bm - 1) / bm;
+        for (int j = 0; j * bm < c; ++j) info[trun + j] = int4{i, run + j * bm, min(bm, c - j * bm), 0};
+        trun += (c + bm - 1) / bm;
       }
+      run += c;
     }
     const int routed = __shfl(incl, WAVE - 1, WAVE);
     const int trouted = __shfl(tincl, WAVE - 1, WAVE);
@@ -135,6 +138,8 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
         tile_prefix[E + 1] = trouted + (S ? (T + bm - 1) / bm : 0);
       }
     }
+    if (tile_prefix && S)  // the shared expert's tiles: all T tokens in order
+      for (int j = lane; j * bm < T; j += WAVE) info[trouted + j] = int4{E, routed + j * bm, min(bm, T - j * bm), 0};
     if (S)
       for (int t = lane; t < T; t += WAVE) sorted_token[routed + t] = t;
     return;

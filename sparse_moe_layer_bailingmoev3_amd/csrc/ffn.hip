@@ -89,7 +89,7 @@ struct TStage {
 // tile) are issued while step s computes, all in one batch, so that waiting for the token
 // tile of the next step (loads complete in issue order) never waits for younger weights.
 template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4, bool PADDED>
-__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nrows, int rb0, int nrb_here,
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                          uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;  // token planes (h hi and lo for down)
@@ -110,7 +110,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int m0, int nr
   const int nsteps = K / KS;                 // k-steps per row block
   const int total_steps = nsteps * nrb_here;  // the pipeline runs through all row blocks
   const bool shared = e == a.E;
-  const int pos0 = a.offsets[e] + m0;
 
   // token tile: per-thread 16-byte pieces (row, col).  Every piece is loaded from a valid
   // address (pieces past the tile or of a position without a token read the tile's first
@@ -402,28 +401,23 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int tsub = w / a.ngroups, grp = w - tsub * a.ngroups;
   const int tile = tsub / subs, sub = tsub - tile * subs;
   const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
-  int lo = 0, hi = a.E + a.S;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_prefix[mid] <= tile) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int m0 = (tile - a.tile_prefix[e]) * a.bm_list + sub * BM;
-  const int cnt = a.offsets[e + 1] - a.offsets[e];
-  if (m0 >= cnt) return;
-  const int nrows = min(BM, cnt - m0);
+  const int4 info = ((const int4*)(a.tile_prefix + tile_info_offset(a.E)))[tile];
+  const int e = info.x, m0 = sub * BM;
+  if (m0 >= info.z) return;
+  const int nrows = min(BM, info.z - m0);
   if constexpr (FMT == FMT_MXFP4) {
     if (e < a.E) {
-      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, m0, nrows, rb0, nrb_here, lds);
+      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, lds);
       return;
     }
   }
-  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, m0, nrows, rb0, nrb_here, lds);
+  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, lds);
 }
 
-// single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan
+// single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan, and the
+// tile records after it (n = E + S experts, the tile_info block at tile_info_offset(n - S))
 __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int n, int bm,
-                                                         int32_t* __restrict__ tile_prefix) {
+                                                         int32_t* __restrict__ tile_prefix, int info_off) {
   const int lane = threadIdx.x;
   const int per = (n + WAVE - 1) / WAVE;
   const int b = lane * per, e = min(n, b + per);
@@ -437,8 +431,11 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
   }
   int run = incl - sum;
   if (lane == 0) tile_prefix[0] = 0;
+  int4* info = (int4*)(tile_prefix + info_off);
   for (int i = b; i < e; ++i) {
-    run += (offsets[i + 1] - offsets[i] + bm - 1) / bm;
+    const int o = offsets[i], c = offsets[i + 1] - o;
+    for (int j = 0; j * bm < c; ++j) info[run + j] = int4{i, o + j * bm, min(bm, c - j * bm), 0};
+    run += (c + bm - 1) / bm;
     tile_prefix[i + 1] = run;
   }
 }
@@ -555,7 +552,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   hipError_t err = hipSuccess;
   if (p.tiles) {
     if (!tiles_ready) {
-      launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix);
+      launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix, tile_info_offset(E));
       err = hipGetLastError();
       if (tr) tr->mark("expert_tiles", s);
       if (err != hipSuccess) return err;
@@ -564,7 +561,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                                    shared_limit, h_hi, h_lo, y, s, tr);
   }
   if (!tiles_ready) {
-    launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix);
+    launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix, tile_info_offset(E));
     err = hipGetLastError();
     if (tr) tr->mark("expert_tiles", s);
   }

@@ -101,7 +101,12 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.counts = take((E + 1) * 4);
   L.counts_out = take((E + 1) * 4);
   L.offsets = take((E + 2) * 4);
-  L.tile_prefix = take((E + 2) * 4);
+  // the FFN tile prefix and, after it, one 16-byte record per tile of the plan
+  L.tile_prefix = take(((size_t)moe::tile_info_offset((int)E) +
+                        4 * (size_t)moe::ffn_plan(T, (int)K, (int)E, (int)S,
+                                                  c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4
+                                                                                               : moe::FMT_BF16,
+                                                  (int)H, (int)I).max_tiles) * 4);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
   L.sorted_token = take(P * 4);

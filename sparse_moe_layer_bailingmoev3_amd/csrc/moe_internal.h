@@ -9,6 +9,12 @@ namespace moe {
 
 enum { FMT_BF16 = 0, FMT_MXFP4 = 1 };
 
+// The FFN tile list: tile_prefix[0 .. E+1] (tiles of the experts before e), then, from this
+// offset (in int32, 16-byte aligned), one record per tile: {expert, its first sorted
+// position, its rows, 0}, so that a workgroup finds its tile with one load instead of a
+// binary search.  Whoever writes the prefix writes the records too.
+constexpr int tile_info_offset(int E) { return (E + 2 + 3) / 4 * 4; }
+
 // Optional per-kernel event trace: events[0] is recorded before the first launch,
 // events[i+1] right after the i-th kernel (a NULL slot records nothing); names[i] names that
 // kernel.  Independently, kernel `tindex` can be timed by events bound to its own dispatch

@@ -422,12 +422,16 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
       }
     }
     int run = incl - sum, trun = tincl - tsum;
+    int4* info = fd.tile_prefix ? (int4*)(fd.tile_prefix + tile_info_offset(E)) : nullptr;
     for (int i = b; i < en; ++i) {
       const int c = cnt[i];
       offs[i] = run;
       fd.offsets[i] = run;
       fd.counts_out[i] = c;
-      if (fd.tile_prefix) fd.tile_prefix[i] = trun;
+      if (fd.tile_prefix) {
+        fd.tile_prefix[i] = trun;
+        for (int j = 0; j * fd.bm < c; ++j) info[trun + j] = int4{i, run + j * fd.bm, min(fd.bm, c - j * fd.bm), 0};
+      }
       run += c;
       trun += (c + fd.bm - 1) / fd.bm;
     }
@@ -442,6 +446,9 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
         fd.tile_prefix[E + 1] = trouted + (fd.S ? (T + fd.bm - 1) / fd.bm : 0);
       }
     }
+    if (fd.tile_prefix && fd.S)  // the shared expert's tiles: all T tokens in order
+      for (int j = lane; j * fd.bm < T; j += 64)
+        info[trouted + j] = int4{E, routed + j * fd.bm, min(fd.bm, T - j * fd.bm), 0};
   }
   __syncthreads();
   // each (token, slot): its position is the expert's offset plus the number of the expert's
