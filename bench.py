@@ -246,6 +246,56 @@ def measure_dense(T, H, I, steps, warmup, hip):
             "hbm_GBps": round(hbm, 1), "bf16_TFLOPs": round(mfma, 1), "algorithmic_bytes": byts, "flops": flops}
 
 
+def measure_stack(shape, L, steps, warmup, hip):
+    """L MoE layers of the same shape, each with its own weights and its own N(0,1) input
+    (drawn on the GPU from the same distributions as the single layer), run back to back: a
+    decode step through a stack of distinct layers, so that no layer's weights can be found
+    in a cache from the step before.  The layers are not chained: without the model's
+    residual stream and norms, one layer's raw output (RMS ~0.03) would route every token of
+    the next layer to the same few experts.  Returns ms per step and per layer."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    E, H, I, T = shape.E, shape.H, shape.I, shape.T
+    g = torch.Generator(device="cuda").manual_seed(1)
+
+    def normal_bf16(*dims):
+        out = torch.empty(dims, dtype=torch.bfloat16, device="cuda")
+        for i in range(0, dims[0], 64):  # in slices: no full-size fp32 temporary
+            out[i:i + 64] = torch.randn((min(64, dims[0] - i),) + dims[1:], generator=g, device="cuda").mul_(0.02)
+        return out
+
+    cfg = cfg_for(shape)
+    layers = []
+    for _ in range(L):
+        w = moe.MoEExpertWeights(normal_bf16(E, I, H), normal_bf16(E, I, H), normal_bf16(E, H, I),
+                                 shared_gate=normal_bf16(shape.I_s, H), shared_up=normal_bf16(shape.I_s, H),
+                                 shared_down=normal_bf16(H, shape.I_s))
+        rw = torch.randn((E, H), generator=g, device="cuda").mul_(0.02)
+        b = torch.rand((E,), generator=g, device="cuda").mul_(0.2).sub_(0.1)
+        layers.append((rw, b, w))
+    xs = [torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(L)]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        for l, (rw, b, w) in enumerate(layers):
+            moe.moe_forward(cfg, T, xs[l], rw, b, w, out, None, None, None, ws)
+
+    for _ in range(warmup):
+        step()
+    a, e = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for _ in range(steps):
+        step()
+    hip.record(e, stream)
+    ms = hip.elapsed_ms(a, e) / steps
+    return {"workload": f"decode through {L} distinct layers: T={T}, hidden {H}, {E} experts", "layers": L,
+            "ms_per_step": round(ms, 4), "ms_per_layer": round(ms / L, 4),
+            "tokens_per_s_per_layer": round(T / (ms / L * 1e-3), 1), "weights_GB": round(L * expert_bytes(shape) * E / 1e9, 1)}
+
+
 def roofline(shape, r, workload=None):
     """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
     bound to its dispatch in every step of the timed region.
@@ -453,6 +503,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
+    ap.add_argument("--stack", type=int, default=0, metavar="L",
+                    help="instead: decode (T=64) through L distinct layers, each with its own weights (L <= 32)")
     ap.add_argument("--dense", type=int, default=0, metavar="I",
                     help="instead: the dense SwiGLU FFN (moe_dense_ffn) of intermediate size I at T=1, 64, 512, 8192")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
@@ -471,6 +523,14 @@ def main():
     from synthetic import CONFIGS, gen_experts
     import sparse_moe_layer_bailingmoev3_amd as moe
     moe.load_library()  # no fallback: fails loudly without the HIP library
+    if args.stack:
+        if not 1 <= args.stack <= 32:
+            sys.exit("--stack takes 1 to 32 layers (6 GB of weights each)")
+        hip = Hip()
+        res = measure_stack(CONFIGS["decode"], args.stack, max(args.steps, 5), args.warmup, hip)
+        print(json.dumps({"metric": "MoE-layer tokens/s through a stack of distinct layers", "dtype": "bf16",
+                          "data": "synthetic (seeded, drawn on the GPU)", "n_gpus": 1, **res}), flush=True)
+        return
     if args.dense:
         hip = Hip()
         H = CONFIGS["decode"].H
