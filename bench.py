@@ -216,24 +216,30 @@ def time_bias_update(shape, counts, hip, reps=200):
 
 def measure_dense(T, H, I, steps, warmup, hip):
     """The dense SwiGLU FFN (moe_dense_ffn) at T tokens: seeded bf16 inputs, `steps` timed calls
-    between two events.  Algorithmic bytes: the three weight matrices once (3*I*H*2) + x read
-    + out written; flops 6*T*H*I."""
+    between two events, the calls cycling through enough weight sets (600 MB or more in all)
+    that none is still in the 256 MB Infinity Cache from its previous call, as in a model
+    whose other layers run in between.  Algorithmic bytes: the three weight matrices once
+    (3*I*H*2) + x read + out written; flops 6*T*H*I."""
     import torch
     import sparse_moe_layer_bailingmoev3_amd as moe
     g = torch.Generator(device="cuda").manual_seed(0)
     x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
-    wg, wu = (torch.randn((I, H), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16) for _ in range(2))
-    wd = torch.randn((H, I), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    nsets = max(2, -(-600_000_000 // (3 * I * H * 2)))
+    sets = []
+    for _ in range(nsets):
+        wg, wu = (torch.randn((I, H), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16) for _ in range(2))
+        wd = torch.randn((H, I), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+        sets.append((wg, wu, wd))
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_dense_ffn_workspace_size(H, I, T), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(warmup):
-        moe.moe_dense_ffn(H, I, 0.0, T, x, wg, wu, wd, out, ws)
+    for i in range(warmup):
+        moe.moe_dense_ffn(H, I, 0.0, T, x, *sets[i % nsets], out, ws)
     a, b = hip.event(), hip.event()
     torch.cuda.synchronize()
     hip.record(a, stream)
-    for _ in range(steps):
-        moe.moe_dense_ffn(H, I, 0.0, T, x, wg, wu, wd, out, ws)
+    for i in range(steps):
+        moe.moe_dense_ffn(H, I, 0.0, T, x, *sets[i % nsets], out, ws)
     hip.record(b, stream)
     ms = hip.elapsed_ms(a, b) / steps
     byts = 3 * I * H * 2 + 2 * T * H * 2
@@ -243,7 +249,8 @@ def measure_dense(T, H, I, steps, warmup, hip):
     frac = hbm / HBM_PEAK_GBS if bound == "hbm" else mfma / BF16_PEAK_TFLOPS
     return {"workload": f"dense SwiGLU FFN: T={T}, hidden {H}, intermediate {I}", "value": round(T / (ms * 1e-3), 1),
             "unit": "tokens/s", "ms_per_call": round(ms, 4), "bound": bound, "frac": round(frac, 4),
-            "hbm_GBps": round(hbm, 1), "bf16_TFLOPs": round(mfma, 1), "algorithmic_bytes": byts, "flops": flops}
+            "hbm_GBps": round(hbm, 1), "bf16_TFLOPs": round(mfma, 1), "algorithmic_bytes": byts, "flops": flops,
+            "weight_sets": nsets}
 
 
 def measure_stack(shape, L, steps, warmup, hip):
@@ -506,7 +513,9 @@ def main():
     ap.add_argument("--stack", type=int, default=0, metavar="L",
                     help="instead: decode (T=64) through L distinct layers, each with its own weights (L <= 32)")
     ap.add_argument("--dense", type=int, default=0, metavar="I",
-                    help="instead: the dense SwiGLU FFN (moe_dense_ffn) of intermediate size I at T=1, 64, 512, 8192")
+                    help="instead: the dense SwiGLU FFN (moe_dense_ffn) of intermediate size I")
+    ap.add_argument("--dense-tokens", default="1,64,512,8192", metavar="T,T,...",
+                    help="token counts of the --dense measurement")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ from the rocprofv3 runs in DIR and exit")
@@ -534,7 +543,7 @@ def main():
     if args.dense:
         hip = Hip()
         H = CONFIGS["decode"].H
-        res = [measure_dense(T, H, args.dense, max(args.steps, 10), args.warmup, hip) for T in (1, 64, 512, 8192)]
+        res = [measure_dense(T, H, args.dense, max(args.steps, 10), args.warmup, hip) for T in map(int, args.dense_tokens.split(","))]
         print(json.dumps({"metric": "dense SwiGLU FFN tokens/s", "dtype": "bf16", "data": "synthetic (seeded)",
                           "n_gpus": 1, "results": res}), flush=True)
         return

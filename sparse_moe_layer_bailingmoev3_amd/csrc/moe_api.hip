@@ -368,6 +368,14 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
   Layout L;
   if ((st = check_ws(&dc, T, ws, ws_bytes, &L)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (moe::dense_ffn_small_supported(T, hidden_size, intermediate_size)) {
+    hipError_t e = moe::launch_dense_ffn_small((const uint16_t*)x, (const uint16_t*)gate, (const uint16_t*)up,
+                                               (const uint16_t*)down, (int)T, hidden_size, intermediate_size,
+                                               dc.swiglu_limit, (uint16_t*)at(ws, L.h_hi), (uint16_t*)at(ws, L.h_lo),
+                                               (uint16_t*)out, s);
+    if (e != hipSuccess) return hip_fail(e, "dense FFN launch");
+    return MOE_OK;
+  }
   int32_t* offsets = (int32_t*)at(ws, L.offsets);
   int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);

@@ -131,6 +131,15 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
                                    int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
                                    uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr);
 
+// ---- dense FFN for few tokens (dense_ffn.hip) -----------------------------------
+// gate/up then down, each workgroup's waves splitting the reduction; h planes [T,I] in the
+// caller's workspace, the bf16 output written by the down kernel (no dispatch, no combine)
+constexpr int DENSE_SMALL_MAX_T = 16;
+bool dense_ffn_small_supported(int64_t T, int H, int I);
+hipError_t launch_dense_ffn_small(const uint16_t* x, const uint16_t* gate, const uint16_t* up, const uint16_t* down,
+                                  int T, int H, int I, float limit, uint16_t* h_hi, uint16_t* h_lo, uint16_t* out,
+                                  hipStream_t s);
+
 // ---- combine -----------------------------------------------------------------
 hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,
                           int K, int H, int S, uint16_t* out, hipStream_t s, Tracer* tr = nullptr);
