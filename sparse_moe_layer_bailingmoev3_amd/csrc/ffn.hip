@@ -54,6 +54,7 @@ struct FfnArgs {
   int rbw;                      // row blocks one workgroup streams back to back
   int ngroups;                  // ceil(nrb / rbw): row-block groups per tile
   int bm_list;                  // positions per tile of the device tile list (a multiple of 16*MF)
+  int group_major;              // 1: work id = group * tiles + tile (else tile * groups + group)
   float limit, shared_limit;
 };
 
@@ -390,15 +391,26 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
 
   // device work list: work id -> (tile, sub-tile, row-block group); consecutive work ids
   // run on the same XCD.  A tile of the list holds bm_list positions and splits into
-  // bm_list / BM sub-tiles of this kernel's size (empty sub-tiles exit at once).
+  // bm_list / BM sub-tiles of this kernel's size (empty sub-tiles exit at once).  Tile-major
+  // order puts the row-block groups of a tile side by side (they share its token rows in
+  // L2); group-major order, for a single weight set, the tiles of a row-block group (they
+  // share its weight rows).
   const int subs = a.bm_list / BM;
-  const int total = a.tile_prefix[a.E + a.S] * subs * a.ngroups;
+  const int ntsub = a.tile_prefix[a.E + a.S] * subs;
+  const int total = ntsub * a.ngroups;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
   if (slot >= per_xcd) return;
   const int w = (blockIdx.x & 7) * per_xcd + slot;
   if (w >= total) return;
-  const int tsub = w / a.ngroups, grp = w - tsub * a.ngroups;
+  int tsub, grp;
+  if (a.group_major) {
+    grp = w / ntsub;
+    tsub = w - grp * ntsub;
+  } else {
+    tsub = w / a.ngroups;
+    grp = w - tsub * a.ngroups;
+  }
   const int tile = tsub / subs, sub = tsub - tile * subs;
   const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
   const int4 info = ((const int4*)(a.tile_prefix + tile_info_offset(a.E)))[tile];
@@ -523,6 +535,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // (measured against the small tiles: T = 1024 (16 per expert) 1.094 -> 1.074 ms, T = 1536
   // 1.297 -> 1.215, T = 2048 1.446 -> 1.294, T = 4096 1.89 -> 1.57)
   p.tiles = fmt == FMT_BF16 && avg > 12 && ffn_tiles_supported(H, I);
+  p.group_major = false;
   if (p.tiles) p.mf = 16;
   p.bm = 16 * p.mf;
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
@@ -532,13 +545,15 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   if (E == 1 && S == 0 && avg <= 1024) {
     // a single expert (the dense FFN) has no experts to spread over the CUs: tiles of at most
     // T/8 tokens and one row block per workgroup, so that token tiles x row blocks fill the
-    // chip (each tile re-reads the weights, mostly from the Infinity Cache)
+    // chip; up to 512 tokens the tiles of one row block run side by side on one XCD
+    // (group-major work order), so that its weight rows come from L2 for all but the first
     p.mf = avg <= 128 ? 1 : avg <= 256 ? 2 : avg <= 512 ? 4 : 8;
     p.mf_gate_up = p.mf;
     p.mf_down = std::min(p.mf, 4);
     p.tiles = false;
     p.bm = 16 * p.mf;
     p.rbw_gate_up = p.rbw_down = 1;
+    p.group_major = avg <= 512;  // measured: T = 64 88 -> 83 us, 128 158 -> 144, 512 206 -> 198; 1024 279 -> 282
   }
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
@@ -581,6 +596,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   dn.K = I; dn.N = H;
 
   gu.bm_list = dn.bm_list = p.bm;
+  gu.group_major = dn.group_major = p.group_major ? 1 : 0;
   err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr);
   if (err != hipSuccess) return err;
   return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr);

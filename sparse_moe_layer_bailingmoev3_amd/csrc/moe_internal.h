@@ -115,6 +115,7 @@ struct FfnPlan {
   int bm;      // tokens per tile = 16 * mf
   int rbw_gate_up, rbw_down;  // 128-row weight blocks per workgroup
   bool tiles;  // use the 256-token tile kernel (bm = 256)
+  bool group_major;  // work order: the tiles of one row-block group consecutive (one weight set)
   int64_t max_tiles;
 };
 FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I);
