@@ -55,6 +55,8 @@ struct FfnArgs {
   int ngroups;                  // ceil(nrb / rbw): row-block groups per tile
   int bm_list;                  // positions per tile of the device tile list (a multiple of 16*MF)
   int group_major;              // 1: work id = group * tiles + tile (else tile * groups + group)
+  int dense;                    // 1: one weight set and the identity permutation (a dense FFN): tiles
+                                // follow from T, no dispatch arrays are read, down writes bf16 out [T,N]
   float limit, shared_limit;
 };
 
@@ -127,7 +129,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
     bool ok = c < CHUNKS && row < nrows;
     const int prow = row < nrows ? row : 0;
     if (MODE == MODE_GATEUP) {
-      const int tok = a.sorted_token[pos0 + prow];
+      const int tok = a.dense ? pos0 + prow : a.sorted_token[pos0 + prow];
       ok = ok && (unsigned)tok < (unsigned)a.T;
       tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + col;
     } else {
@@ -319,6 +321,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
             }
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
             *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          } else if (a.dense) {
+            const floatx4 v = acc[0][f][mf];
+            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
             *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][mf];
           }
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   // L2); group-major order, for a single weight set, the tiles of a row-block group (they
   // share its weight rows).
   const int subs = a.bm_list / BM;
-  const int ntsub = a.tile_prefix[a.E + a.S] * subs;
+  const int ntsub = (a.dense ? (a.T + a.bm_list - 1) / a.bm_list : a.tile_prefix[a.E + a.S]) * subs;
   const int total = ntsub * a.ngroups;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
@@ -413,7 +418,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   }
   const int tile = tsub / subs, sub = tsub - tile * subs;
   const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
-  const int4 info = ((const int4*)(a.tile_prefix + tile_info_offset(a.E)))[tile];
+  const int4 info = a.dense ? int4{0, tile * a.bm_list, min(a.bm_list, a.T - tile * a.bm_list), 0}
+                            : ((const int4*)(a.tile_prefix + tile_info_offset(a.E)))[tile];
   const int e = info.x, m0 = sub * BM;
   if (m0 >= info.z) return;
   const int nrows = min(BM, info.z - m0);
@@ -542,12 +548,14 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // pipeline start; few tokens per expert keep more, shorter workgroups for parallelism
   p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
   p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one row block per workgroup (measured)
-  if (E == 1 && S == 0 && avg <= 1024) {
+  if (E == 1 && S == 0 && avg <= 4096) {
     // a single expert (the dense FFN) has no experts to spread over the CUs: tiles of at most
     // T/8 tokens and one row block per workgroup, so that token tiles x row blocks fill the
     // chip; up to 512 tokens the tiles of one row block run side by side on one XCD
-    // (group-major work order), so that its weight rows come from L2 for all but the first
-    p.mf = avg <= 128 ? 1 : avg <= 256 ? 2 : avg <= 512 ? 4 : 8;
+    // (group-major work order), so that its weight rows come from L2 for all but the first.
+    // Above 4096 tokens the 256-position tile kernel is faster (measured at hidden 2560,
+    // intermediate 6912: T = 4096 0.76 against 0.90 ms, T = 8192 1.47 against 1.26 ms).
+    p.mf = avg <= 128 ? 1 : avg <= 256 ? 2 : avg <= 512 ? 4 : avg <= 2048 ? 8 : 16;
     p.mf_gate_up = p.mf;
     p.mf_down = std::min(p.mf, 4);
     p.tiles = false;
@@ -600,6 +608,26 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr);
   if (err != hipSuccess) return err;
   return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr);
+}
+
+hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
+                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
+                                  uint16_t* h_lo, uint16_t* out, hipStream_t s) {
+  if (p.tiles) return hipErrorInvalidValue;  // the 256-position tile kernel reads the dispatch arrays
+  FfnArgs gu{};
+  gu.act = x; gu.w0 = gate; gu.w1 = up; gu.out = h_hi; gu.out_lo = h_lo;
+  gu.T = T; gu.E = 1; gu.S = 0; gu.K = H; gu.N = I;
+  gu.limit = limit;
+  gu.bm_list = p.bm;
+  gu.group_major = p.group_major ? 1 : 0;
+  gu.dense = 1;
+  FfnArgs dn = gu;
+  dn.act = h_hi; dn.act_lo = h_lo; dn.out_lo = nullptr; dn.w0 = down; dn.w1 = nullptr; dn.out = out;
+  dn.K = I; dn.N = H;
+  const int64_t ntiles = ((int64_t)T + p.bm - 1) / p.bm;
+  hipError_t err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, FMT_BF16, ntiles, s, nullptr);
+  if (err != hipSuccess) return err;
+  return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, FMT_BF16, ntiles, s, nullptr);
 }
 
 }  // namespace moe

@@ -420,7 +420,12 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   gu.sw0 = (const uint16_t*)w.sh_gate; gu.sw1 = (const uint16_t*)w.sh_up;
   gu.out = h_hi; gu.out_lo = h_lo;
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
-  gu.nrb = I / (GU_RFR * 16); gu.rbw = std::min(gu.nrb, GU_RBW); gu.ngroups = (gu.nrb + gu.rbw - 1) / gu.rbw;
+  // one weight set (a dense FFN): one row block per item, for twice the items (a single
+  // expert has few token tiles to spread over the CUs)
+  const bool single = E == 1 && S == 0 && items_fit(I, GU_RFR * 16, 1, H, GU_NST - 1) &&
+                      items_fit(H, DN_RFR * 16, 1, I, DN_NST - 1);
+  gu.nrb = I / (GU_RFR * 16); gu.rbw = std::min(gu.nrb, single ? 1 : GU_RBW);
+  gu.ngroups = (gu.nrb + gu.rbw - 1) / gu.rbw;
   gu.limit = limit; gu.shared_limit = shared_limit;
   gu.interleave = GU_INTERLEAVE;
 
@@ -430,7 +435,8 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   dn.out = y; dn.out_lo = nullptr;
   dn.K = I; dn.N = H;
   dn.interleave = DN_INTERLEAVE;
-  dn.nrb = H / (DN_RFR * 16); dn.rbw = std::min(dn.nrb, DN_RBW); dn.ngroups = (dn.nrb + dn.rbw - 1) / dn.rbw;
+  dn.nrb = H / (DN_RFR * 16); dn.rbw = std::min(dn.nrb, single ? 1 : DN_RBW);
+  dn.ngroups = (dn.nrb + dn.rbw - 1) / dn.rbw;
 
   // workgroups that each take several work items: four per CU (one is resident at a time, as
   // each holds 96 KB of LDS), so a CU whose items ran fast picks up the next workgroup;

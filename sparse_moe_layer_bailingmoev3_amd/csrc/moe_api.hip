@@ -376,6 +376,16 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
     if (e != hipSuccess) return hip_fail(e, "dense FFN launch");
     return MOE_OK;
   }
+  const moe::FfnPlan plan = moe::ffn_plan(T, 1, 1, 0, moe::FMT_BF16, hidden_size, intermediate_size);
+  if (!plan.tiles) {
+    // the expert FFN kernels with the tiles computed from T (no dispatch, no combine)
+    hipError_t e = moe::launch_dense_ffn_tiled(plan, (const uint16_t*)x, (const uint16_t*)gate, (const uint16_t*)up,
+                                               (const uint16_t*)down, (int)T, hidden_size, intermediate_size,
+                                               dc.swiglu_limit, (uint16_t*)at(ws, L.h_hi), (uint16_t*)at(ws, L.h_lo),
+                                               (uint16_t*)out, s);
+    if (e != hipSuccess) return hip_fail(e, "dense FFN launch");
+    return MOE_OK;
+  }
   int32_t* offsets = (int32_t*)at(ws, L.offsets);
   int32_t* sorted_token = (int32_t*)at(ws, L.sorted_token);
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);

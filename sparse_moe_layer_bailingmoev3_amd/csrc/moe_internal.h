@@ -125,6 +125,13 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr);
 
+// a dense FFN (one weight set, every token, weight 1) on the expert FFN kernels without the
+// dispatch and combine: tiles follow from T, down writes the bf16 output [T,H] (plan from
+// ffn_plan(T, 1, 1, 0, FMT_BF16, H, I) without the 256-position tile kernel)
+hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
+                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
+                                  uint16_t* h_lo, uint16_t* out, hipStream_t s);
+
 // 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles
 bool ffn_tiles_supported(int H, int I);
 hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
