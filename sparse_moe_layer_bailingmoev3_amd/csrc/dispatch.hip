@@ -3,14 +3,19 @@
 // lqnn.cn, section 三.2, ends with 8 experts per token; each expert then serves its tokens).
 //
 // Deterministic and independent of the order of atomics:
-//   1. mark     one bit per (expert, token) in a bitmap [E][ceil(T/32)] and a histogram of
-//               expert counts (atomicOr / atomicAdd on integers: the final values do not
-//               depend on their order).  The fused forward does this inside the router's
-//               top-k kernel and clears the bitmap inside the router's logits kernel.
-//   2. finish   one wave per expert: its offset is the sum of the counts before it; it walks
-//               its bitmap row in ascending token order and writes sorted_token and
-//               inv_perm.  One more wave writes the offsets, the shared expert's identity
-//               block and, for the fused forward, the expert FFN's tile prefix.
+//   1. mark     one bit per (expert, token) in a bitmap [E][ceil(T/32)] (atomicOr on
+//               integers: the final bits do not depend on the order).  moe_dispatch marks
+//               here and counts with atomicAdd; the fused forward marks inside the router's
+//               top-k kernel (after its logits kernel cleared the bitmap), and the histogram
+//               is then the popcount of each bitmap row (dispatch_count_kernel).  Up to 256
+//               tokens the fused forward does all of the dispatch in the top-k kernel's last
+//               workgroup (router.hip) instead.
+//   2. finish   one wave per (expert, 2048-token chunk of its row): the chunk's first
+//               position is the sum of the counts before the expert plus the row's earlier
+//               bits; it walks the set bits in ascending token order and writes sorted_token
+//               and inv_perm.  One more wave writes the offsets, the counts with the shared
+//               expert's entry, the shared expert's identity block and, for the fused
+//               forward, the expert FFN's tile prefix and tile records.
 #include "moe_common.h"
 #include "moe_internal.h"
 

@@ -12,10 +12,11 @@
 //     one wave); two steps of loads are kept in flight;
 //   * the token rows (gathered x rows for gate/up, contiguous h rows for down) are the b
 //     operand, staged once per workgroup in double-buffered LDS and shared by all waves;
-//   * the reduction dimension is consumed KS values per step; lane group q of a 16-row
-//     operand owns the contiguous slice [q*KS/4, (q+1)*KS/4) of the step and MFMA sub-step s
-//     takes its s-th 8-value piece (the same permutation of k for both operands, so the
-//     dot products are unchanged and every lane loads one contiguous run);
+//   * the reduction dimension is consumed KS values per step.  bf16: MFMA sub-step s takes
+//     k = 32s + 8q .. +7 for lane group q of both operands, so one load instruction covers
+//     64 contiguous bytes of each of its 16 rows; MXFP4: lane group q owns the 32-value
+//     scale block q of a step and sub-step s its s-th 8-value piece, for both operands (the
+//     same permutation of k on both sides leaves the dot products unchanged);
 //   * gate and up share the token operand; SwiGLU and the clamp run on the accumulators;
 //     the activation h is stored as two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
 //     and the down projection runs one MFMA per plane, so h keeps ~16 significand bits

@@ -6,7 +6,7 @@
 // beside the MFMA work:
 //   * a workgroup (8 waves) owns a tile of up to BM = 16*TPW*8 sorted positions of one
 //     expert; wave w owns 16*TPW of them and all rows of the current row block
-//     (64 gate + 64 up rows, or 128 down rows), so each weight byte is read from HBM once
+//     (128 gate + 128 up rows, or 256 down rows), so each weight byte is read from HBM once
 //     per workgroup;
 //   * weights, which every wave uses, move through an NSTAGE-deep ring in LDS with direct
 //     global->LDS loads; a wave's token values, used by that wave only, go straight into

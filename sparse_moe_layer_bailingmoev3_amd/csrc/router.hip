@@ -6,7 +6,7 @@
 // largest in-group maximum and pick the top-k experts inside them; section 四: the router
 // runs in fp32, the chosen scores are renormalised and scaled by routed_scaling_factor.
 //
-// Two kernels:
+// Kernels:
 //   router_logits_kernel  fp32-accurate logits on bf16 MFMA.  x is bf16, so splitting each
 //                         fp32 router weight exactly into three bf16 pieces (hi + mid + lo,
 //                         8 significand bits each) makes every product x * piece exact in
@@ -15,8 +15,12 @@
 //                         split-precision idea of Markidis et al. 2018 / Ootomo & Yokota
 //                         2022).  The hidden dimension may be split across workgroups for
 //                         small token counts; partial sums are added later in a fixed order.
+//   router_logits_kwaves_kernel  the same logits for up to 256 tokens: 16-expert workgroups
+//                         whose four waves split their slice of the hidden dimension.
 //   router_topk_kernel    one wave per token: sigmoid, bias, group max, group ranking and the
-//                         top-k selection entirely in registers with wave shuffles.
+//                         top-k selection entirely in registers with wave shuffles; for up to
+//                         256 tokens the last workgroup to finish also builds the dispatch.
+//   expert_bias_update_kernel  the sign-rule bias step from a step's expert counts.
 #include "moe_common.h"
 #include "moe_internal.h"
 
