@@ -294,7 +294,8 @@ def test_expert_bias_update_matches_oracle(name):
                                          (512, 768, 29, 0.003), (512, 384, 32, 0.0), (384, 2048, 50, 0.0),
                                          (512, 384, 64, 0.002), (2560, 6912, 64, 0.0), (512, 384, 70, 0.0),
                                          (512, 640, 300, 0.002), (512, 384, 1500, 0.0), (2560, 6912, 1100, 0.0),
-                                         (512, 384, 3000, 0.0), (512, 384, 4100, 0.002)])
+                                         (512, 384, 3000, 0.0), (512, 384, 4100, 0.002), (512, 384, 129, 0.0),
+                                         (512, 384, 257, 0.0), (512, 640, 513, 0.002), (384, 384, 2049, 0.0)])
 def test_dense_ffn_matches_oracle(H, I, T, limit):
     """Dense SwiGLU FFN (the layers before the MoE stack) against the oracle's SwiGLU FFN in
     float64: every output row at small sizes, 64 sampled rows at the full hidden size."""
