@@ -163,9 +163,10 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
  * page gives no intermediate size, so it is a parameter, and the FFN is read as the experts'
  * own SwiGLU form):  out[t] = ( silu(x[t] gate^T) * (x[t] up^T) ) down^T, the activation
  * clamped to +-swiglu_limit when it is > 0, fp32 accumulation, one rounding to bf16.
- * Up to 16 tokens it runs on two kernels of its own (gate/up, then down writing out); up to
+ * Up to 10 tokens it runs on two kernels of its own (gate/up, then down writing out); up to
  * 4096, on the kernels of moe_expert_ffn with tiles computed from T and the output written by
- * the down GEMM; above, as a layer with a single routed expert that every token takes with
+ * the down GEMM (or, up to 512 tokens, by a last kernel adding the down GEMM's split
+ * reduction in order); above, as a layer with a single routed expert that every token takes with
  * weight 1, on the kernels of moe_expert_ffn and moe_combine.  All paths round h the same way
  * (two bf16 planes) and sum in a fixed order, so they differ only by summation order.
  *   x device bf16 [T,H]; gate, up device bf16 [I,H]; down device bf16 [H,I]; out device

@@ -2,7 +2,7 @@
 // routing walk-through page, lqnn.cn, section 二, first_k_dense_replace; the same SwiGLU form as
 // the experts, with the optional clamp of section 四).
 //
-// With one weight set and at most 16 tokens the work is a stream of the three weight matrices,
+// With one weight set and at most 10 tokens the work is a stream of the three weight matrices,
 // and parallelism can only come from the weight rows and the reduction dimension.  Design for
 // gfx950:
 //   * a workgroup owns a block of 16 weight rows (of gate and up together, or of down) and the
@@ -23,8 +23,9 @@
 //     [q*KS/4, (q+1)*KS/4) of a step and MFMA sub-step s takes its s-th 8-value piece, the
 //     same for both operands, so every lane loads one contiguous run per row.
 // Every wave reads the token rows of its own slice, so the token traffic grows with T (down
-// reads two h planes per token); above 16 tokens the expert FFN kernels, which share a token
-// tile between the waves of a workgroup through LDS, measured faster.
+// reads two h planes per token); above 10 tokens the expert FFN kernels, which share a token
+// tile between the waves of a workgroup through LDS and split the down reduction over
+// workgroups, measured faster.
 #include "moe_common.h"
 #include "moe_internal.h"
 

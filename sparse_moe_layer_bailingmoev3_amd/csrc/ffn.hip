@@ -58,6 +58,8 @@ struct FfnArgs {
   int group_major;              // 1: work id = group * tiles + tile (else tile * groups + group)
   int dense;                    // 1: one weight set and the identity permutation (a dense FFN): tiles
                                 // follow from T, no dispatch arrays are read, down writes bf16 out [T,N]
+  int ksplit;                   // workgroups splitting the reduction (down of a dense FFN; else 1)
+  float* part;                  // ksplit > 1: fp32 partial sums [ksplit,T,N], added in order later
   float limit, shared_limit;
 };
 
@@ -94,7 +96,7 @@ struct TStage {
 // tile of the next step (loads complete in issue order) never waits for younger weights.
 template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4, bool PADDED>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
-                                         uint16_t* lds) {
+                                         int ksp, uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;  // token planes (h hi and lo for down)
   constexpr int BM = MF * 16;
@@ -111,7 +113,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int K = a.K, N = a.N;
-  const int nsteps = K / KS;                 // k-steps per row block
+  const int kspan = K / a.ksplit, k0 = ksp * kspan;  // this workgroup's part of the reduction
+  const int nsteps = kspan / KS;             // k-steps per row block
   const int total_steps = nsteps * nrb_here;  // the pipeline runs through all row blocks
   const bool shared = e == a.E;
 
@@ -132,10 +135,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
     if (MODE == MODE_GATEUP) {
       const int tok = a.dense ? pos0 + prow : a.sorted_token[pos0 + prow];
       ok = ok && (unsigned)tok < (unsigned)a.T;
-      tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + col;
+      tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + k0 + col;
     } else {
-      tsrc[0][i] = a.act + (size_t)(pos0 + prow) * K + col;
-      tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + col;
+      tsrc[0][i] = a.act + (size_t)(pos0 + prow) * K + k0 + col;
+      tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + k0 + col;
     }
     tvalid[i] = ok;
   }
@@ -156,13 +159,13 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
       if constexpr (FP4) {
         const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / 2);
         const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
-        wq[m][f] = base + row * (K / 2) + q * (KS / 8);
-        wsc[m][f] = sbase + row * (K / 32) + q * (KS / 128);
+        wq[m][f] = base + row * (K / 2) + k0 / 2 + q * (KS / 8);
+        wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + q * (KS / 128);
         wp[m][f] = nullptr;
       } else {
         const uint16_t* base = shared ? (const uint16_t*)(m == 0 ? a.sw0 : a.sw1)
                                       : (const uint16_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * K;
-        wp[m][f] = base + row * K + q * 8;
+        wp[m][f] = base + row * K + k0 + q * 8;
         wq[m][f] = nullptr;
         wsc[m][f] = nullptr;
       }
@@ -322,6 +325,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
             }
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
             *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          } else if (a.ksplit > 1) {
+            *(floatx4*)(a.part + ((size_t)ksp * a.T + pos0 + j) * N + ncol + f * 16) = acc[0][f][mf];
           } else if (a.dense) {
             const floatx4 v = acc[0][f][mf];
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -403,12 +408,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   // share its weight rows).
   const int subs = a.bm_list / BM;
   const int ntsub = (a.dense ? (a.T + a.bm_list - 1) / a.bm_list : a.tile_prefix[a.E + a.S]) * subs;
-  const int total = ntsub * a.ngroups;
+  const int total = ntsub * a.ngroups * a.ksplit;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
   if (slot >= per_xcd) return;
-  const int w = (blockIdx.x & 7) * per_xcd + slot;
-  if (w >= total) return;
+  const int wk = (blockIdx.x & 7) * per_xcd + slot;
+  if (wk >= total) return;
+  // the parts of a split reduction are consecutive work ids
+  const int w = wk / a.ksplit, ksp = wk - w * a.ksplit;
   int tsub, grp;
   if (a.group_major) {
     grp = w / ntsub;
@@ -426,11 +433,22 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int nrows = min(BM, info.z - m0);
   if constexpr (FMT == FMT_MXFP4) {
     if (e < a.E) {
-      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, lds);
+      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
       return;
     }
   }
-  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, lds);
+  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
+}
+
+// out[i] = bf16(sum over s of part[s][i]), the parts of a split reduction added in order;
+// four values per thread
+__global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict__ part, int ksplit, int64_t n4,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  floatx4 v = ((const floatx4*)part)[i];
+  for (int s = 1; s < ksplit; ++s) v += ((const floatx4*)part)[s * n4 + i];
+  ((u32x2*)out)[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // single wave: tiles of expert i = ceil(count_i / bm); tile_prefix = exclusive scan, and the
@@ -488,16 +506,17 @@ template <int MF, int MODE, int FMT>
 hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Tracer* tr) {
   using C = FfnCfg<MF, FMT, MODE>;
   constexpr int ROWS = C::NW * C::RF * 16;  // weight rows per block of each matrix
-  if (a.bm_list % (16 * MF) || a.N % ROWS) return hipErrorInvalidValue;
+  if (a.bm_list % (16 * MF) || a.N % ROWS || a.ksplit < 1 || a.K % a.ksplit) return hipErrorInvalidValue;
+  const int kspan = a.K / a.ksplit;
   a.nrb = a.N / ROWS;
   a.rbw = std::min(a.nrb, rbw);
   a.ngroups = (a.nrb + a.rbw - 1) / a.rbw;
-  int64_t work = max_tiles * (a.bm_list / (16 * MF)) * a.ngroups;
+  int64_t work = max_tiles * (a.bm_list / (16 * MF)) * a.ngroups * a.ksplit;
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  if (a.K % C::KS == 0)
+  if (kspan % C::KS == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
-  else if (C::KS_ALT != C::KS && a.K % C::KS_ALT == 0)
+  else if (C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT>, dim3((unsigned)grid), dim3(C::NW * 64), s,
            a);
   else
@@ -543,6 +562,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // 1.297 -> 1.215, T = 2048 1.446 -> 1.294, T = 4096 1.89 -> 1.57)
   p.tiles = fmt == FMT_BF16 && avg > 12 && ffn_tiles_supported(H, I);
   p.group_major = false;
+  p.ksplit_down = 1;
   if (p.tiles) p.mf = 16;
   p.bm = 16 * p.mf;
   // row blocks streamed back to back by one workgroup: long-lived workgroups amortise the
@@ -550,19 +570,34 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   p.rbw_gate_up = p.mf >= 4 ? 3 : 1;
   p.rbw_down = p.mf >= 4 ? 5 : 1;  // decode: one row block per workgroup (measured)
   if (E == 1 && S == 0 && avg <= 4096) {
-    // a single expert (the dense FFN) has no experts to spread over the CUs: tiles of at most
-    // T/8 tokens and one row block per workgroup, so that token tiles x row blocks fill the
-    // chip; up to 512 tokens the tiles of one row block run side by side on one XCD
-    // (group-major work order), so that its weight rows come from L2 for all but the first.
-    // Above 4096 tokens the 256-position tile kernel is faster (measured at hidden 2560,
-    // intermediate 6912: T = 4096 0.76 against 0.90 ms, T = 8192 1.47 against 1.26 ms).
-    p.mf = avg <= 128 ? 1 : avg <= 256 ? 2 : avg <= 512 ? 4 : avg <= 2048 ? 8 : 16;
+    // a single expert (the dense FFN) has no experts to spread over the CUs: one row block per
+    // workgroup, so that token tiles x row blocks fill the chip, with tiles of 16 to 256 tokens
+    // growing with T (measured at hidden 2560, intermediate 6912, against 16-token tiles up to
+    // 128 tokens: T = 64 67 -> 49 us, T = 128 125 -> 78; against 64-token tiles up to 512:
+    // T = 512 175 -> 141 us); up to 512 tokens the tiles of one row block run side by side on
+    // one XCD (group-major work order), so that its weight rows come from L2 for all but the
+    // first.  Above 4096 tokens the 256-position tile kernel is faster (T = 4096 0.76 against
+    // 0.90 ms, T = 8192 1.47 against 1.26 ms).
+    p.mf = avg <= 32 ? 1 : avg <= 128 ? 2 : avg <= 256 ? 4 : avg <= 2048 ? 8 : 16;
     p.mf_gate_up = p.mf;
     p.mf_down = std::min(p.mf, 4);
     p.tiles = false;
     p.bm = 16 * p.mf;
     p.rbw_gate_up = p.rbw_down = 1;
     p.group_major = avg <= 512;  // measured: T = 64 88 -> 83 us, 128 158 -> 144, 512 206 -> 198; 1024 279 -> 282
+    // few tokens: the down GEMM (H / 64 or H / 128 row blocks per tile) also splits its
+    // reduction over up to DENSE_MAX_KSPLIT workgroups, toward ~768 workgroups; the split
+    // must leave a whole number of 128-value (one 16-token fragment) or 64-value steps
+    if (avg <= DENSE_KSPLIT_MAX_T) {
+      const int64_t tiles = (T + 16 * p.mf_down - 1) / (16 * p.mf_down);
+      const int rows = p.mf_down == 1 ? 64 : 128, ks_step = p.mf_down == 1 ? 128 : 64;
+      const int64_t want = std::max<int64_t>(1, 768 / std::max<int64_t>(1, tiles * (H / rows)));
+      for (int d = (int)std::min<int64_t>(want, DENSE_MAX_KSPLIT); d > 1; --d)
+        if (I % d == 0 && (I / d) % ks_step == 0) {
+          p.ksplit_down = d;
+          break;
+        }
+    }
   }
   const int64_t pairs = T * K + T * S;
   p.max_tiles = pairs / p.bm + std::min<int64_t>(E, T * K) + S + 1;
@@ -597,6 +632,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   gu.sw0 = w.sh_gate; gu.sw1 = w.sh_up; gu.out = h_hi; gu.out_lo = h_lo;
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
   gu.limit = limit; gu.shared_limit = shared_limit;
+  gu.ksplit = 1;
 
   FfnArgs dn = gu;
   dn.act = h_hi; dn.act_lo = h_lo; dn.sorted_token = nullptr; dn.out_lo = nullptr;
@@ -613,8 +649,9 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
 
 hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
                                   const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
-                                  uint16_t* h_lo, uint16_t* out, hipStream_t s) {
+                                  uint16_t* h_lo, float* part, uint16_t* out, hipStream_t s) {
   if (p.tiles) return hipErrorInvalidValue;  // the 256-position tile kernel reads the dispatch arrays
+  if (p.ksplit_down > 1 && !part) return hipErrorInvalidValue;
   FfnArgs gu{};
   gu.act = x; gu.w0 = gate; gu.w1 = up; gu.out = h_hi; gu.out_lo = h_lo;
   gu.T = T; gu.E = 1; gu.S = 0; gu.K = H; gu.N = I;
@@ -622,13 +659,21 @@ hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uin
   gu.bm_list = p.bm;
   gu.group_major = p.group_major ? 1 : 0;
   gu.dense = 1;
+  gu.ksplit = 1;
   FfnArgs dn = gu;
   dn.act = h_hi; dn.act_lo = h_lo; dn.out_lo = nullptr; dn.w0 = down; dn.w1 = nullptr; dn.out = out;
   dn.K = I; dn.N = H;
+  dn.ksplit = p.ksplit_down;
+  dn.part = part;
   const int64_t ntiles = ((int64_t)T + p.bm - 1) / p.bm;
   hipError_t err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, FMT_BF16, ntiles, s, nullptr);
   if (err != hipSuccess) return err;
-  return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, FMT_BF16, ntiles, s, nullptr);
+  err = launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, FMT_BF16, ntiles, s, nullptr);
+  if (err != hipSuccess || dn.ksplit == 1) return err;
+  const int64_t n4 = (int64_t)T * H / 4;
+  hipLaunchKernelGGL(ksplit_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)part,
+                     dn.ksplit, n4, out);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -326,6 +326,15 @@ moe_config_t dense_config(int32_t H, int32_t I, float limit) {
   return c;
 }
 
+// the layer's workspace; with a split down reduction its partial sums start at the y region
+// (the last one) and may run past it
+size_t dense_ws_bytes(const moe_config_t* dc, int64_t T) {
+  const Layout L = layout(dc, T);
+  const moe::FfnPlan p = moe::ffn_plan(T, 1, 1, 0, moe::FMT_BF16, dc->hidden_size, dc->moe_intermediate_size);
+  if (p.ksplit_down <= 1) return L.total;
+  return std::max(L.total, L.y + align256((size_t)p.ksplit_down * T * dc->hidden_size * 4));
+}
+
 moe_status_t validate_dense(int32_t H, int32_t I, float limit, int64_t T) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)T);
   if (T > (int64_t)((1u << 31) - 1) / 2) return fail(MOE_ERR_UNSUPPORTED, "T = %lld is too large", (long long)T);
@@ -346,7 +355,7 @@ moe_status_t moe_dense_ffn_workspace_size(int32_t hidden_size, int32_t intermedi
   if (st != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes must not be NULL");
   const moe_config_t dc = dense_config(hidden_size, intermediate_size, 0.0f);
-  *bytes = layout(&dc, T).total;
+  *bytes = dense_ws_bytes(&dc, T);
   return MOE_OK;
 }
 
@@ -367,6 +376,9 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
   if ((st = check_weights(&dc, &w)) != MOE_OK) return st;
   Layout L;
   if ((st = check_ws(&dc, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if (ws_bytes < dense_ws_bytes(&dc, T))
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", ws_bytes, dense_ws_bytes(&dc, T),
+                (long long)T);
   hipStream_t s = (hipStream_t)stream;
   if (moe::dense_ffn_small_supported(T, hidden_size, intermediate_size)) {
     hipError_t e = moe::launch_dense_ffn_small((const uint16_t*)x, (const uint16_t*)gate, (const uint16_t*)up,
@@ -382,7 +394,7 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
     hipError_t e = moe::launch_dense_ffn_tiled(plan, (const uint16_t*)x, (const uint16_t*)gate, (const uint16_t*)up,
                                                (const uint16_t*)down, (int)T, hidden_size, intermediate_size,
                                                dc.swiglu_limit, (uint16_t*)at(ws, L.h_hi), (uint16_t*)at(ws, L.h_lo),
-                                               (uint16_t*)out, s);
+                                               (float*)at(ws, L.y), (uint16_t*)out, s);
     if (e != hipSuccess) return hip_fail(e, "dense FFN launch");
     return MOE_OK;
   }

@@ -116,6 +116,7 @@ struct FfnPlan {
   int rbw_gate_up, rbw_down;  // 128-row weight blocks per workgroup
   bool tiles;  // use the 256-token tile kernel (bm = 256)
   bool group_major;  // work order: the tiles of one row-block group consecutive (one weight set)
+  int ksplit_down;   // workgroups splitting the down reduction (a dense FFN with few tokens; else 1)
   int64_t max_tiles;
 };
 FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I);
@@ -128,9 +129,13 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
 // a dense FFN (one weight set, every token, weight 1) on the expert FFN kernels without the
 // dispatch and combine: tiles follow from T, down writes the bf16 output [T,H] (plan from
 // ffn_plan(T, 1, 1, 0, FMT_BF16, H, I) without the 256-position tile kernel)
+// part: fp32 [p.ksplit_down, T, H] when p.ksplit_down > 1 (the partial sums of the split down
+// reduction, added in order by a last kernel)
+constexpr int DENSE_MAX_KSPLIT = 16;
+constexpr int64_t DENSE_KSPLIT_MAX_T = 512;
 hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
                                   const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
-                                  uint16_t* h_lo, uint16_t* out, hipStream_t s);
+                                  uint16_t* h_lo, float* part, uint16_t* out, hipStream_t s);
 
 // 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles
 bool ffn_tiles_supported(int H, int I);
@@ -142,7 +147,7 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
 // ---- dense FFN for few tokens (dense_ffn.hip) -----------------------------------
 // gate/up then down, each workgroup's waves splitting the reduction; h planes [T,I] in the
 // caller's workspace, the bf16 output written by the down kernel (no dispatch, no combine)
-constexpr int DENSE_SMALL_MAX_T = 16;
+constexpr int DENSE_SMALL_MAX_T = 10;  // measured crossover with the expert kernels (T = 8: 35.6 against 38.5 us, 16: 45.4 against 40.2)
 bool dense_ffn_small_supported(int64_t T, int H, int I);
 hipError_t launch_dense_ffn_small(const uint16_t* x, const uint16_t* gate, const uint16_t* up, const uint16_t* down,
                                   int T, int H, int I, float limit, uint16_t* h_hi, uint16_t* h_lo, uint16_t* out,

@@ -284,18 +284,20 @@ def test_expert_bias_update_matches_oracle(name):
     assert np.array_equal(bias.cpu().numpy().view(np.uint32), oracle.update_expert_bias(want, np.full(s.E + 1, 5), gamma).view(np.uint32))
 
 
-# up to 16 tokens the dense FFN runs its own kernels (the reduction split over the waves of a
+# up to 10 tokens the dense FFN runs its own kernels (the reduction split over the waves of a
 # workgroup; 32-value steps where the preferred step does not divide a wave's slice, as at
-# H = 384 and I = 640); up to 4096 tokens the expert FFN kernels with tiles computed from T
-# (no dispatch or combine launches; 256-token tiles above 2048); beyond, the 256-position tile
-# kernel as a one-expert layer
-@pytest.mark.parametrize("H,I,T,limit", [(512, 384, 1, 0.0), (384, 640, 13, 0.0), (512, 768, 16, 0.003),
-                                         (2560, 6912, 1, 0.0), (2560, 6912, 16, 0.0), (512, 768, 17, 0.0),
+# H = 384 and I = 640); up to 4096 tokens the expert FFN kernels with tiles computed from T (16
+# to 256 tokens, no dispatch or combine; up to 512 tokens the down reduction split over
+# workgroups and summed in order by a last kernel); beyond, the 256-position tile kernel as a
+# one-expert layer
+@pytest.mark.parametrize("H,I,T,limit", [(512, 384, 1, 0.0), (384, 640, 9, 0.0), (512, 768, 10, 0.003),
+                                         (2560, 6912, 1, 0.0), (2560, 6912, 8, 0.0), (512, 768, 11, 0.0),
+                                         (2560, 6912, 16, 0.0), (384, 640, 13, 0.0), (512, 768, 17, 0.0),
                                          (512, 768, 29, 0.003), (512, 384, 32, 0.0), (384, 2048, 50, 0.0),
                                          (512, 384, 64, 0.002), (2560, 6912, 64, 0.0), (512, 384, 70, 0.0),
-                                         (512, 640, 300, 0.002), (512, 384, 1500, 0.0), (2560, 6912, 1100, 0.0),
-                                         (512, 384, 3000, 0.0), (512, 384, 4100, 0.002), (512, 384, 129, 0.0),
-                                         (512, 384, 257, 0.0), (512, 640, 513, 0.002), (384, 384, 2049, 0.0)])
+                                         (512, 384, 129, 0.0), (512, 384, 257, 0.0), (512, 640, 300, 0.002),
+                                         (512, 640, 513, 0.002), (512, 384, 1500, 0.0), (2560, 6912, 1100, 0.0),
+                                         (384, 384, 2049, 0.0), (512, 384, 3000, 0.0), (512, 384, 4100, 0.002)])
 def test_dense_ffn_matches_oracle(H, I, T, limit):
     """Dense SwiGLU FFN (the layers before the MoE stack) against the oracle's SwiGLU FFN in
     float64: every output row at small sizes, 64 sampled rows at the full hidden size."""
