@@ -143,7 +143,8 @@ def test_forward_tiles_unsupported_shape():
     check_forward(host_case(CONFIGS["tiny"].with_(hidden_size=384), seed=15, T=1000))
 
 
-@pytest.mark.parametrize("T", [40, 1000])
+# T = 40: 16-token tiles; 600 (75 tokens per expert): 64-token tiles; 1000: 128-token tiles
+@pytest.mark.parametrize("T", [40, 600, 1000])
 def test_forward_tiny_mxfp4(T):
     s = CONFIGS["tiny"].with_(weight_format="mxfp4")
     bf = gen_experts(CONFIGS["tiny"], seed=16)
