@@ -52,7 +52,7 @@ def check_forward(c, rows=None, tol=TOL_BF16, dev=None):
 # ----------------------------------------------------------------------------------
 # tiny layer: every token, every stage
 # ----------------------------------------------------------------------------------
-@pytest.mark.parametrize("T", [32, 1, 17, 63, 64, 65, 200, 1000])
+@pytest.mark.parametrize("T", [32, 1, 17, 63, 64, 65, 200, 256, 257, 1000])  # 256 / 257: the last fused dispatch and the first separate one
 def test_forward_tiny(T):
     check_forward(host_case(CONFIGS["tiny"], seed=0, T=T))
 
