@@ -485,20 +485,24 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 // MFMA.  16-token bf16 tiles (decode) take 256-value steps, two in flight, in 64-row
 // workgroups: each weight row then goes out in 512-byte runs (measured: decode gate/up 311 ->
 // 297 us, down 161 -> 159 us against 64-value steps); so does the gate/up of 32-token tiles
-// (T = 1024: 683 -> 655 us; their down GEMM measured slower that way).  Where K is not a
-// multiple of 256 they fall back to 128-value steps, four in flight (KS_ALT, D_ALT).
+// (T = 1024: 683 -> 655 us; their down GEMM measured slower that way).  The down GEMM of
+// 16-token tiles takes 384-value steps, so that a 768-long reduction is two steps, both in
+// flight from the start (decode down 155.4 -> 153.9 us).  Where K is not a multiple of the
+// step they fall back to 256-value steps (KS_MID), then to 128-value steps, four in flight
+// (KS_ALT, D_ALT).
 template <int MF, int FMT, int MODE> struct FfnCfg {
   static constexpr bool FP4 = FMT == FMT_MXFP4;
   static constexpr bool DOWN = MODE == MODE_DOWN;
   static constexpr bool WIDE = !FP4 && (MF == 1 || (MF == 2 && !DOWN));
   static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
   static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
-  static constexpr int KS = FP4 ? 128 : WIDE ? 256 : 64;
+  static constexpr int KS = FP4 ? 128 : WIDE ? ((MF == 1 && DOWN) ? 384 : 256) : 64;
   static constexpr int D = WIDE ? 2
                          : MF <= 2 ? (FP4 ? 3 : 4)
                          : MF == 4 ? (FP4 ? 2 : 4)
                          : MF == 8 ? (FP4 ? 2 : (DOWN ? 3 : 4))
                                    : 2;
+  static constexpr int KS_MID = WIDE ? 256 : KS;  // where K is not a multiple of KS
   static constexpr int KS_ALT = WIDE ? 128 : KS, D_ALT = WIDE ? 4 : D;
 };
 
@@ -516,6 +520,9 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   if (grid <= 0) return hipSuccess;
   if (kspan % C::KS == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
+  else if (C::KS_MID != C::KS && kspan % C::KS_MID == 0)
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS_MID>, dim3((unsigned)grid), dim3(C::NW * 64), s,
+           a);
   else if (C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT>, dim3((unsigned)grid), dim3(C::NW * 64), s,
            a);
