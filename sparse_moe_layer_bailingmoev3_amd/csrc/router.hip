@@ -268,6 +268,48 @@ __global__ __launch_bounds__(256) void router_logits_kwaves_kernel(const uint16_
 }
 
 // One token (one wave): the top-k of the routing walk-through page's sections 三.1-三.3.
+// Cross-lane steps of the selection without an LDS round trip.  Inside rows of 16 lanes, DPP
+// moves: quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1, lane ^ 2), row_half_mirror (lane i of 8
+// <-> 7 - i) and row_mirror (lane i of 16 <-> 15 - i); after these four steps of a maximum
+// (exact, so the pairing order does not matter) every lane holds its row's maximum, and the
+// four rows are combined from wave-uniform lane reads.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  return ((uint64_t)readlane_u32((uint32_t)(v >> 32), l) << 32) | readlane_u32((uint32_t)v, l);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// maximum over the wave, the same in every lane
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = max_u64(v, dpp_u64<DPP_XOR1>(v));
+  v = max_u64(v, dpp_u64<DPP_XOR2>(v));
+  v = max_u64(v, dpp_u64<DPP_ROW_HALF_MIRROR>(v));
+  v = max_u64(v, dpp_u64<DPP_ROW_MIRROR>(v));
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+// maximum over aligned groups of lpg consecutive lanes (a power of two), in every lane
+__device__ __forceinline__ float group_max_f32(float v, int lpg) {
+  if (lpg >= 2) v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
+  if (lpg >= 4) v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
+  if (lpg >= 8) v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v))));
+  if (lpg >= 16) v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v))));
+  for (int m = 16; m < lpg; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
+  return v;
+}
+
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ partial, int nsplit, int T, int E,
                                             const float* __restrict__ bias, int G, int TG, int K, int norm,
@@ -300,13 +342,13 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
   float gm = c[0];
 #pragma unroll
   for (int i = 1; i < EPL; ++i) gm = fmaxf(gm, c[i]);
-  for (int m = 1; m < lpg; m <<= 1) gm = fmaxf(gm, __shfl_xor(gm, m, WAVE));
+  gm = group_max_f32(gm, lpg);
 
   // rank of this lane's group among all groups (ties: lower group index first)
   const int g = lane / lpg;
   int rank = 0;
   for (int h = 0; h < G; ++h) {
-    float o = __shfl(gm, h * lpg, WAVE);
+    const float o = __uint_as_float(readlane_u32(__float_as_uint(gm), h * lpg));
     rank += (o > gm) || (o == gm && h < g);
   }
   const bool kept = rank < TG;
@@ -325,7 +367,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    best = wave_max_u64_dpp(best);
     const int idx = (int)(0xFFFFFFFFu - (uint32_t)best);
     const int owner = idx / EPL, slot = idx - owner * EPL;
     float sv = 0.f;
@@ -336,7 +378,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
         if (lane == owner) key[i] = 0ull;
       }
     }
-    sv = __shfl(sv, owner, WAVE);
+    sv = __uint_as_float(readlane_u32(__float_as_uint(sv), owner));
     if (lane == r) {
       my_idx = idx;
       my_s = sv;
@@ -346,7 +388,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ partial, i
   // renormalise (unbiased scores) and scale; write in ascending expert order
   const float sum = wave_sum_f32(lane < K ? my_s : 0.f);
   int pos = 0;
-  for (int j = 0; j < K; ++j) pos += __shfl(my_idx, j, WAVE) < my_idx;
+  for (int j = 0; j < K; ++j) pos += (int)readlane_u32((uint32_t)my_idx, j) < my_idx;
   if (lane < K) {
     const float wv = norm ? (my_s / sum) * scale : my_s * scale;
     topk_idx[(size_t)t * K + pos] = my_idx;
