@@ -143,10 +143,13 @@ def test_forward_tiles_unsupported_shape():
     check_forward(host_case(CONFIGS["tiny"].with_(hidden_size=384), seed=15, T=1000))
 
 
-# T = 40: 16-token tiles; 600 (75 tokens per expert): 64-token tiles; 1000: 128-token tiles
-@pytest.mark.parametrize("T", [40, 600, 1000])
-def test_forward_tiny_mxfp4(T):
+# T = 40: 16-token tiles; 600 (75 tokens per expert): 64-token tiles; 1000: 128-token tiles;
+# the clamped cases put the SwiGLU limits on the MXFP4 epilogue (routed) and the bf16 one (shared)
+@pytest.mark.parametrize("T,limit", [(40, 0.0), (600, 0.0), (1000, 0.0), (40, 0.002), (600, 0.002)])
+def test_forward_tiny_mxfp4(T, limit):
     s = CONFIGS["tiny"].with_(weight_format="mxfp4")
+    if limit:
+        s = s.with_(swiglu_limit=limit, shared_swiglu_limit=1.5 * limit)
     bf = gen_experts(CONFIGS["tiny"], seed=16)
     ex = {}
     for k in ("gate", "up", "down"):
