@@ -115,12 +115,15 @@ moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const 
 
 /* Dispatch: group the T*K (token, slot) pairs by expert.
  *   topk_idx       device int32 [T,K] (each token's K ids distinct and in [0,E);
- *                  out-of-range ids are ignored and their slot gets inv_perm = -1)
+ *                  out-of-range ids are ignored: their slot gets inv_perm = -1 and they
+ *                  are in no count)
  *   expert_counts  device int32 [E+1] tokens per expert; entry E = shared expert (T*S)
- *   expert_offsets device int32 [E+2] exclusive prefix sum of expert_counts
- *   sorted_token   device int32 [P]   positions offsets[e]..offsets[e+1]-1 hold the
+ *   expert_offsets device int32 [E+2] offsets[e] = sum of counts[0..e-1] for e < E;
+ *                  offsets[E] = T*K and offsets[E+1] = T*K + T*S always
+ *   sorted_token   device int32 [P]   positions offsets[e]..offsets[e]+counts[e]-1 hold the
  *                  tokens of expert e in ascending order; the shared expert's block
- *                  holds 0..T-1
+ *                  (from T*K) holds 0..T-1; positions no token fills (those of ignored
+ *                  pairs, at the end of the last routed expert's range) hold -1
  *   inv_perm       device int32 [T,K] sorted position of each (token, slot) */
 moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx,
                           int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,

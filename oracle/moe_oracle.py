@@ -168,19 +168,31 @@ class Dispatch:
 
 
 def dispatch(topk_idx: np.ndarray, num_experts: int, num_shared: int = 1) -> Dispatch:
-    """Group the (token, slot) pairs by expert: positions [offsets[e], offsets[e+1]) hold
-    expert e's tokens in ascending token order; the shared expert is expert E and owns
-    every token in order."""
+    """Group the (token, slot) pairs by expert: positions [offsets[e], offsets[e] + counts[e])
+    hold expert e's tokens in ascending token order; the shared expert is expert E, owns every
+    token in order and always starts at position T*K.
+
+    A pair whose id lies outside [0, E) is ignored (the pages never produce one; this is the
+    library's stated contract for such input): it is in no expert's count, its inv_perm is -1,
+    and the positions it would have taken, counts[:E].sum() .. T*K-1, hold no token (-1) and
+    belong to the last routed expert's range offsets[E-1] .. offsets[E]."""
     T, K = topk_idx.shape
     flat = np.asarray(topk_idx, np.int64).ravel()
+    valid = (flat >= 0) & (flat < num_experts)
     counts = np.zeros(num_experts + 1, dtype=np.int64)
-    counts[:num_experts] = np.bincount(flat, minlength=num_experts)
+    counts[:num_experts] = np.bincount(flat[valid], minlength=num_experts)
     counts[num_experts] = T if num_shared else 0
-    offsets = np.concatenate([[0], np.cumsum(counts)])
-    order = np.argsort(flat, kind="stable")   # by expert, then by flat index t*K+k
-    sorted_token = np.concatenate([order // K, np.arange(T) if num_shared else np.zeros(0, np.int64)])
-    inv = np.empty(T * K, dtype=np.int64)
-    inv[order] = np.arange(T * K)
+    offsets = np.zeros(num_experts + 2, dtype=np.int64)
+    offsets[1:num_experts + 1] = np.cumsum(counts[:num_experts])
+    offsets[num_experts] = T * K
+    offsets[num_experts + 1] = T * K + counts[num_experts]
+    pairs = np.nonzero(valid)[0]
+    order = pairs[np.argsort(flat[pairs], kind="stable")]   # by expert, then by flat index t*K+k
+    routed_tok = np.full(T * K, -1, dtype=np.int64)
+    routed_tok[:order.size] = order // K
+    sorted_token = np.concatenate([routed_tok, np.arange(T) if num_shared else np.zeros(0, np.int64)])
+    inv = np.full(T * K, -1, dtype=np.int64)
+    inv[order] = np.arange(order.size)
     return Dispatch(counts, offsets, sorted_token, inv.reshape(T, K))
 
 

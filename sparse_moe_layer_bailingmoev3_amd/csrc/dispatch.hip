@@ -132,21 +132,25 @@ __global__ __launch_bounds__(256) void dispatch_finish_kernel(const uint32_t* __
       }
       run += c;
     }
+    // the shared expert's block starts at T*K even when pairs were ignored (out-of-range
+    // ids): positions routed .. T*K-1 then hold no token
     const int routed = __shfl(incl, WAVE - 1, WAVE);
     const int trouted = __shfl(tincl, WAVE - 1, WAVE);
+    const int sh0 = T * K;
     if (lane == 0) {
       counts_out[E] = T * S;
-      offsets[E] = routed;
-      offsets[E + 1] = routed + T * S;
+      offsets[E] = sh0;
+      offsets[E + 1] = sh0 + T * S;
       if (tile_prefix) {
         tile_prefix[E] = trouted;
         tile_prefix[E + 1] = trouted + (S ? (T + bm - 1) / bm : 0);
       }
     }
     if (tile_prefix && S)  // the shared expert's tiles: all T tokens in order
-      for (int j = lane; j * bm < T; j += WAVE) info[trouted + j] = int4{E, routed + j * bm, min(bm, T - j * bm), 0};
+      for (int j = lane; j * bm < T; j += WAVE) info[trouted + j] = int4{E, sh0 + j * bm, min(bm, T - j * bm), 0};
+    for (int p = routed + lane; p < sh0; p += WAVE) sorted_token[p] = -1;
     if (S)
-      for (int t = lane; t < T; t += WAVE) sorted_token[routed + t] = t;
+      for (int t = lane; t < T; t += WAVE) sorted_token[sh0 + t] = t;
     return;
   }
   const int e = wv / nchunks, chunk = wv - e * nchunks;

@@ -232,6 +232,7 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
   };
   // at a chunk boundary: when the issue side has finished its item, move it to the next one
   // (item lengths are multiples of D, so items start and end on chunk boundaries)
+  // (called after the compute side has taken any pending item, so `nxt` is free here)
   auto switch_issue = [&]() {
     if (!iss_live || isn < iss.steps) return;
     wi += slots;
@@ -359,7 +360,10 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
       if ((csn + 1) % nsteps == 0 && active) epilogue(csn / nsteps);
       ++csn;
     }
-    switch_issue();
+    // the compute side takes the pending item before the issue side may replace it: the
+    // issue side runs exactly one chunk ahead, so an item it took at the end of the previous
+    // chunk is the one compute starts now, and an item of D steps makes the issue side take
+    // the next one at this same chunk boundary (one pending item is then always enough)
     if (csn == cmp.steps) {
       if (nxt_valid) {
         cmp = nxt;
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
         cmp_live = false;
       }
     }
+    switch_issue();
   }
   wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
 }

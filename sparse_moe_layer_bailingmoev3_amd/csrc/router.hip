@@ -481,12 +481,15 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
       run += c;
       trun += (c + fd.bm - 1) / fd.bm;
     }
+    // the shared expert's block starts at T*K even when pairs were ignored (out-of-range
+    // ids): positions routed .. T*K-1 then hold no token
     const int routed = __shfl(incl, 63, 64), trouted = __shfl(tincl, 63, 64);
+    const int sh0 = T * K;
     if (lane == 0) {
-      offs[E] = routed;
+      offs[E] = sh0;
       fd.counts_out[E] = T * fd.S;
-      fd.offsets[E] = routed;
-      fd.offsets[E + 1] = routed + T * fd.S;
+      fd.offsets[E] = sh0;
+      fd.offsets[E + 1] = sh0 + T * fd.S;
       if (fd.tile_prefix) {
         fd.tile_prefix[E] = trouted;
         fd.tile_prefix[E + 1] = trouted + (fd.S ? (T + fd.bm - 1) / fd.bm : 0);
@@ -494,7 +497,8 @@ __device__ __forceinline__ void fused_dispatch_finish(const FusedDispatch& fd, c
     }
     if (fd.tile_prefix && fd.S)  // the shared expert's tiles: all T tokens in order
       for (int j = lane; j * fd.bm < T; j += 64)
-        info[trouted + j] = int4{E, routed + j * fd.bm, min(fd.bm, T - j * fd.bm), 0};
+        info[trouted + j] = int4{E, sh0 + j * fd.bm, min(fd.bm, T - j * fd.bm), 0};
+    for (int p = routed + lane; p < sh0; p += 64) fd.sorted_token[p] = -1;
   }
   __syncthreads();
   // each (token, slot): its position is the expert's offset plus the number of the expert's

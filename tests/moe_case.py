@@ -36,6 +36,22 @@ class HostCase:
 
     def expert_f64(self, e: int):
         """(gate, up, down) of routed expert e as float64 (decoded from the stored format)."""
+        cache = getattr(self, "_cache", None)
+        if cache is not None and e in cache:
+            return tuple(a.astype(np.float64) for a in cache[e])
+        return self._decode(e)
+
+    def prefetch(self, experts, threads: int = 16):
+        """Decode the given routed experts on a thread pool ahead of an oracle run (the
+        MXFP4 decode takes ~0.25 s per full-size expert); kept as float32, which holds every
+        bf16 and every decoded MXFP4 value exactly."""
+        from concurrent.futures import ThreadPoolExecutor
+        todo = sorted(set(int(e) for e in experts))
+        with ThreadPoolExecutor(threads) as pool:
+            dec = list(pool.map(lambda e: tuple(a.astype(np.float32) for a in self._decode(e)), todo))
+        self._cache = dict(zip(todo, dec))
+
+    def _decode(self, e: int):
         if self.shape.weight_format == "mxfp4":
             ex = self.experts
             return tuple(oracle.mxfp4_dequant(ex[k + "_q"][e], ex[k + "_s"][e]) for k in ("gate", "up", "down"))

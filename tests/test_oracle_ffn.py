@@ -129,6 +129,34 @@ def test_dispatch_definitions():
             assert d.sorted_token[p] == t and d.offsets[idx[t, k]] <= p < d.offsets[idx[t, k] + 1]
 
 
+def test_dispatch_ignores_out_of_range_ids():
+    """Ids outside [0, E) are dropped (the library's contract for such input): they are in no
+    count, their inv_perm is -1, the valid pairs keep their places in expert-then-token order,
+    the gap they leave holds -1 at the end of the routed range, and the shared expert's block
+    still starts at T*K.  Checked against a walk over the pairs written out by hand."""
+    rng = np.random.default_rng(3)
+    T, K, E = 29, 5, 12
+    idx = np.array([rng.choice(E, K, replace=False) for _ in range(T)])
+    drop = rng.random((T, K)) < 0.2
+    idx[drop] = rng.choice([-1, -7, E, E + 3], size=int(drop.sum()))
+    d = dispatch(idx, E, 1)
+    valid = (idx >= 0) & (idx < E)
+    pos = 0
+    for e in range(E):
+        assert d.offsets[e] == pos
+        for t in range(T):
+            for k in range(K):
+                if valid[t, k] and idx[t, k] == e:
+                    assert d.sorted_token[pos] == t and d.inv_perm[t, k] == pos
+                    pos += 1
+        assert d.counts[e] == pos - d.offsets[e]
+    assert pos == valid.sum() < T * K
+    assert np.all(d.sorted_token[pos:T * K] == -1)
+    assert d.offsets[E] == T * K and d.offsets[E + 1] == T * K + T and d.counts[E] == T
+    assert d.sorted_token[T * K:].tolist() == list(range(T))
+    assert np.all(d.inv_perm[~valid] == -1)
+
+
 def test_layer_constants_match_pages():
     with open(os.path.join(GOLDEN, "layer_constants.json")) as f:
         c = json.load(f)

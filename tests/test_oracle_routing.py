@@ -219,3 +219,68 @@ def test_near_tie_gaps_are_reported():
     r = route(l, None, 1, 1, 2, 2.5, True)
     assert r.gap_expert[0] == 0.0 and r.near_tie[0]
     assert r.topk_idx[0].tolist() == [0, 1]
+
+
+# ----------------------------------------------------------------------------------
+# the near-tie detector: hand-worked gaps and brute force
+# ----------------------------------------------------------------------------------
+with open(os.path.join(GOLDEN, "near_tie_hand_cases.json")) as f:
+    TIES = json.load(f)
+
+
+def _num(v):
+    return float("inf") if v == "inf" else float(v)
+
+
+@pytest.mark.parametrize("case", TIES["cases"], ids=[c["name"] for c in TIES["cases"]])
+@pytest.mark.parametrize("decision", ["fp32", "fp64"])
+def test_near_tie_hand_cases(case, decision):
+    """Gaps at the group and expert boundaries and the near-tie flag, worked by hand (the scores
+    are dyadic, so every value is exact): an off-by-one in either boundary, gaps taken on the
+    unbiased score, or an expert gap taken over all experts instead of the kept groups' ones
+    each change at least one expected value."""
+    l = np.array(case["logits"], np.float64)[None, :]
+    r = route(l, np.array(case["bias"], np.float64), case["G"], case["TG"], case["K"], 2.5, True,
+              decision=decision, tie_eps=TIES["tie_eps"])
+    assert r.kept_groups[0].tolist() == case["kept_groups"]
+    assert r.topk_idx[0].tolist() == case["idx"]
+    assert r.gap_group[0] == _num(case["gap_group"])
+    assert r.gap_expert[0] == _num(case["gap_expert"])
+    assert bool(r.near_tie[0]) == case["near_tie"]
+
+
+def _brute_force_gaps(c, G, TG, K):
+    """Gaps from their definition, by enumeration: the kept groups are the TG-subset with the
+    largest sum of group maxima; gap_group = (TG-th largest group maximum) - ((TG+1)-th);
+    gap_expert = (K-th largest biased score among the kept groups' experts) - ((K+1)-th)."""
+    E = len(c)
+    per = E // G
+    gmax = [max(c[g * per:(g + 1) * per]) for g in range(G)]
+    best, kept = None, None
+    for sub in itertools.combinations(range(G), TG):
+        v = sum(gmax[g] for g in sub)
+        if best is None or v > best:
+            best, kept = v, sub
+    ranked = sorted(gmax, reverse=True)
+    gap_g = ranked[TG - 1] - ranked[TG] if TG < G else float("inf")
+    cand = sorted((c[e] for g in kept for e in range(g * per, (g + 1) * per)), reverse=True)
+    gap_e = cand[K - 1] - cand[K] if K < len(cand) else float("inf")
+    return gap_g, gap_e
+
+
+@pytest.mark.parametrize("E,G,TG,K", TINY_SHAPES)
+def test_brute_force_gaps(E, G, TG, K):
+    # scores on a coarse grid, so that near and exact ties at both boundaries occur often
+    rng = np.random.default_rng(2000 + E * 7 + G + TG * 13 + K)
+    T = 80
+    l = rng.integers(-4, 5, size=(T, E)) * 0.25
+    b = rng.integers(-2, 3, size=E) * 2.0 ** -22
+    r = route(l, b, G, TG, K, 2.5, True, decision="fp32")
+    n_tie = 0
+    for t in range(T):
+        gg, ge = _brute_force_gaps(list(r.choice[t]), G, TG, K)
+        assert r.gap_group[t] == gg and r.gap_expert[t] == ge, (t, r.choice[t])
+        assert bool(r.near_tie[t]) == (min(gg, ge) < 1e-6)
+        n_tie += bool(r.near_tie[t])
+    if TG < G or K < TG * E // G:
+        assert 0 < n_tie < T  # both outcomes exercised
