@@ -223,6 +223,22 @@ moe_status_t moe_forward_timed(const moe_config_t* cfg, int64_t T, const void* x
                                void* ws, size_t ws_bytes, void* stream, int32_t kernel_index,
                                void* start_event, void* stop_event);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments and results as moe_forward (bit for bit), minus ws/ws_bytes: the workspace
+ * is a static device array inside the library, 64 MiB on each GPU the library runs on, held
+ * until the process ends (its device address is looked up on the first call on a device,
+ * which must be current).  The call allocates nothing.  T whose workspace
+ * (moe_workspace_size) exceeds 64 MiB is rejected with MOE_ERR_WORKSPACE before anything is
+ * enqueued: for the full-size layer (hidden 2560, 512 experts, intermediate 768) that is T
+ * above about 500 tokens.  Every call on one GPU uses the same array and leaves its contents
+ * behind (each call rewrites what it reads), so calls that overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race. */
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                 const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                                 int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                                 void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status_t status);
 

@@ -18,7 +18,7 @@ from typing import Optional
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
            "moe_forward_timed", "moe_update_expert_bias", "moe_dense_ffn_workspace_size", "moe_dense_ffn",
-           "moe_status_string",
+           "moe_forward_noalloc", "moe_status_string",
            "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "EXPORTED_SYMBOLS"]
 
 MOE_WEIGHTS_BF16 = 0
@@ -26,7 +26,8 @@ MOE_WEIGHTS_MXFP4 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_update_expert_bias",
-                    "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_status_string", "moe_last_error")
+                    "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_forward_noalloc", "moe_status_string",
+                    "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -93,6 +94,7 @@ def load_library():
         "moe_update_expert_bias": [C, P, P, ctypes.c_float, P],
         "moe_dense_ffn_workspace_size": [ctypes.c_int32, ctypes.c_int32, I64, ctypes.POINTER(SZ)],
         "moe_dense_ffn": [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I64, P, P, P, P, P, P, SZ, P],
+        "moe_forward_noalloc": [C, I64, P, P, P, W, P, P, P, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -216,3 +218,12 @@ def moe_dense_ffn(hidden_size, intermediate_size, swiglu_limit, T, x, gate, up, 
     p, n = _ws(ws)
     _check(load_library().moe_dense_ffn(hidden_size, intermediate_size, float(swiglu_limit), T, _ptr(x), _ptr(gate),
                                         _ptr(up), _ptr(down), _ptr(out), p, n, _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, T, x, router_w, expert_bias, weights: MoEExpertWeights, out, topk_idx_out=None,
+                        topk_w_out=None, expert_counts_out=None, stream=None):
+    """moe_forward on the library's static 64 MiB device scratch instead of a caller workspace
+    (for callers that cannot allocate); rejects T whose workspace does not fit."""
+    _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
+                                              ctypes.byref(weights.struct), _ptr(out), _ptr(topk_idx_out),
+                                              _ptr(topk_w_out), _ptr(expert_counts_out), _stream(stream)))

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -13,6 +14,15 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Device scratch of moe_forward_noalloc: one copy per GPU the library runs on, held until the
+// process ends.  In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (g_scratch_ptr).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
 
 moe_status_t fail(moe_status_t st, const char* fmt, ...) {
   char buf[512];
@@ -531,6 +541,41 @@ moe_status_t moe_forward_timed(const moe_config_t* cfg, int64_t T, const void* x
   if (st == MOE_OK && !tr.timed)
     return fail(MOE_ERR_INVALID_ARG, "kernel_index %d: the forward launched %d kernels", kernel_index, tr.n);
   return st;
+}
+
+
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                 const float* expert_bias, const moe_expert_weights_t* weights, void* out,
+                                 int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                                 void* stream) {
+  g_last_error.clear();
+  moe_status_t st = validate_config(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(cfg, T).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: T=%lld needs %zu bytes of scratch, the static scratch holds %zu; "
+                "use moe_forward with a caller workspace", (long long)T, need, NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond %d", dev, MAX_DEVICES);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      // first call on this device (it is current): the device address of its copy
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p || ((uintptr_t)p & 255u)) return fail(MOE_ERR_HIP, "scratch has no 256-byte aligned device address");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return forward_impl(cfg, T, x, router_w, expert_bias, weights, out, topk_idx_out, topk_w_out, expert_counts_out,
+                      ws, NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"
