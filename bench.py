@@ -182,12 +182,39 @@ def measure(shape, d, steps, warmup, hip):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = hip.elapsed_ms(t_start, t_end) / steps
-    dom_ms = float(np.mean([hip.elapsed_ms(*timed[s]) for s in range(steps)]))
+    dom_all = [hip.elapsed_ms(*timed[s]) for s in range(steps)]
+    dom_ms = float(np.mean(dom_all))
+    # per-step spread, outside the timed region: the same forwards with one event between
+    # consecutive steps (each event adds a few microseconds of queue time to its step)
+    marks = [hip.event() for _ in range(steps + 1)]
+    hip.record(marks[0], stream)
+    for s in range(steps):
+        moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, None, None, None, ws)
+        hip.record(marks[s + 1], stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([hip.elapsed_ms(marks[s], marks[s + 1]) for s in range(steps)])
     # routing of the last step (for algorithmic bytes)
     moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
     torch.cuda.synchronize()
     counts = cnt.cpu().numpy()
-    return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, dom=dom, dom_ms=dom_ms, counts=counts, out=out)
+    return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, dom=dom, dom_ms=dom_ms, counts=counts, out=out,
+                idx=idx.cpu().numpy(), dom_dist=_dist(dom_all), step_dist=_dist(step_ms))
+
+
+def _dist(v):
+    v = np.asarray(v, np.float64)
+    return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4), "n": int(v.size)}
+
+
+def load_stats(shape, counts):
+    """Routing load of one step from the per-expert counts: touched experts, max and mean
+    count, and the share of assignments taken by the busiest 10 % of experts (the skewed
+    workload is built so that it exceeds one half)."""
+    c = np.sort(np.asarray(counts[:shape.E], np.int64))[::-1]
+    total = int(c.sum())
+    return {"touched_experts": int((c > 0).sum()), "max_count": int(c[0]), "mean_count": round(total / shape.E, 2),
+            "top10pct_share": round(float(c[: max(1, shape.E // 10)].sum()) / max(1, total), 4)}
 
 
 def time_bias_update(shape, counts, hip, reps=200):
@@ -303,7 +330,7 @@ def measure_stack(shape, L, steps, warmup, hip):
             "tokens_per_s_per_layer": round(T / (ms / L * 1e-3), 1), "weights_GB": round(L * expert_bytes(shape) * E / 1e9, 1)}
 
 
-def roofline(shape, r, workload=None):
+def roofline(shape, r, workload=None, measured=None):
     """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
     bound to its dispatch in every step of the timed region.
 
@@ -337,12 +364,66 @@ def roofline(shape, r, workload=None):
     else:
         rl = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                   frac=round(tflops / BF16_PEAK_TFLOPS, 4))
-    rl.update(kernel=dom, kernel_ms=round(ms, 4), algorithmic_bytes=int(byts), bf16_flops=flops,
-              touched_experts=touched, traffic=recorded_traffic(workload or shape.name, dom))
+    rl.update(kernel=dom, kernel_ms=round(ms, 4), kernel_ms_dist=r.get("dom_dist"), algorithmic_bytes=int(byts),
+              bf16_flops=flops, touched_experts=touched, traffic=recorded_traffic(workload or shape.name, dom))
+    if measured:
+        # HBM-bound kernels here mostly read: the measured read rate is their ceiling
+        rl["frac_of_measured"] = round(gbs / measured["read_GBps"], 4) if rl["bound"] == "hbm" else \
+            round(tflops / measured["bf16_mfma_TFLOPs"], 4)
     return rl
 
 
-def layer_summary(shape, r):
+def measured_peaks(hip, nbytes=1 << 30, n=4096):
+    """Achievable rates on this GPU, beside the nominal peaks, from the probe kernels of
+    libmoe_probe.so (package/probe/peak_probe.hip): a plain 1 GiB HBM read, a plain 1 GiB copy
+    (bytes read + written) and a loop of independent bf16 16x16x32 MFMAs, each the best over
+    a few grid sizes and 3 runs, timed with events; plus torch's bf16 GEMM (hipBLASLt) at
+    n x n x n as a library reference."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(moe.lib_path()), "libmoe_probe.so"))
+    stream = torch.cuda.current_stream().cuda_stream
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    b = torch.empty_like(a)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    n16 = nbytes // 16
+    V, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+
+    def best(launch, grids, reps=3):
+        t = 1e9
+        for g in grids:
+            launch(g)  # warm
+            for _ in range(reps):
+                e0, e1 = hip.event(), hip.event()
+                hip.record(e0, stream)
+                assert launch(g) == 0
+                hip.record(e1, stream)
+                t = min(t, hip.elapsed_ms(e0, e1))
+        return t
+    grids = (1024, 2048, 4096, 8192)
+    t_read = best(lambda g: lib.moe_probe_read(V(a.data_ptr()), S(n16), V(sink.data_ptr()), I(g), V(stream)), grids)
+    t_copy = best(lambda g: lib.moe_probe_copy(V(a.data_ptr()), V(b.data_ptr()), S(n16), I(g), V(stream)), grids)
+    iters = 2000
+    t_mfma, g_mfma = 1e9, 0
+    for g in (512, 1024, 2048):
+        t = best(lambda gg: lib.moe_probe_mfma_bf16(I(iters), I(gg), V(sink.data_ptr()), V(stream)), (g,))
+        if g * 4 * iters * 8 * 16384 * 2 / t > g_mfma * 4 * iters * 8 * 16384 * 2 / max(t_mfma, 1e-9):
+            t_mfma, g_mfma = t, g
+    mfma_tflops = g_mfma * 4 * iters * 8 * 16384 * 2.0 / (t_mfma * 1e-3) / 1e12
+    A = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    B = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    C = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    t_mm = best(lambda g: (torch.matmul(A, B, out=C), 0)[1], (0,), reps=5)
+    del a, b, A, B, C
+    return {"read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "copy_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "bf16_mfma_TFLOPs": round(mfma_tflops, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, 1),
+            "note": "probe kernels (1 GiB read; 1 GiB copy, read + written bytes; independent bf16 MFMA loop) "
+                    "and torch bf16 matmul 4096^3 (hipBLASLt); best over grids and runs"}
+
+
+def layer_summary(shape, r, measured=None):
     """Whole-layer figures: algorithmic bytes of the step and fractions of both peaks."""
     counts = r["counts"]
     E, H, I, K, T = shape.E, shape.H, shape.I, shape.K, shape.T
@@ -351,9 +432,27 @@ def layer_summary(shape, r):
     byts = touched * expert_bytes(shape) + S * 3 * H * I * 2 + E * H * 4 + E * 4 + 2 * T * H * 2
     flops = 6.0 * H * I * (T * K + T * S)
     ms = r["wall_ms"]
+    hbm_t, mfma_t = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
     return dict(algorithmic_bytes=int(byts), hbm_frac=round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                 bf16_flops=flops, mfma_frac=round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
-                router_fp32_flops=2.0 * T * H * E, touched_experts=touched)
+                binding_roofline_frac=round(max(hbm_t, mfma_t) / (ms * 1e-3), 4),
+                hbm_frac_of_measured_read=round(byts / (ms * 1e-3) / 1e9 / measured["read_GBps"], 4) if measured else None,
+                router_fp32_flops=2.0 * T * H * E, touched_experts=touched, step_ms_dist=r.get("step_dist"),
+                load=load_stats(shape, counts))
+
+
+def routing_check(shape, d, idx_gpu):
+    """The oracle's routing of every token of a measured step against the GPU's (part of the
+    CPU leg): tokens whose group or expert score gap is below 1e-6 are near ties, counted and
+    excused; every other token must route identically."""
+    import oracle
+    T = shape.T
+    x = oracle.bf16_to_f64(d["x_bits"])
+    r = oracle.route(oracle.router_logits(x, d["router_w_np"]), d["bias_np"], shape.G, shape.TG, shape.K,
+                     shape.routed_scaling_factor, shape.norm_topk_prob, tie_eps=1e-6)
+    diff = (np.asarray(idx_gpu) != r.topk_idx).any(1)
+    return {"tokens": T, "near_ties": int(r.near_tie.sum()), "differ_at_near_ties": int((diff & r.near_tie).sum()),
+            "differ_elsewhere": int((diff & ~r.near_tie).sum()), "tie_eps": 1e-6}
 
 
 def cpu_baseline(shape, d, experts, max_tokens):
@@ -415,10 +514,12 @@ def _step(sym: str):
 
 
 def profile_commands(workload: str, out: str = "$OUT"):
-    b = f"python3 $R/bench.py --workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-prefill --copy-probe"
+    b = (f"python3 $R/bench.py --workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-secondary "
+         f"--no-peaks --copy-probe")
     return [f"rocprofv3 --kernel-trace --stats -f csv -d {out}/kt -o kt -- {b}",
             f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/fetch -o fetch -- {b}",
             f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/write -o write -- {b}",
+            f"rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict -f csv -d {out}/util -o util -- {b}",
             f"python3 $R/bench.py --summarize {out} --workload {workload}"]
 
 
@@ -447,6 +548,9 @@ def summarize(src: str, workload: str):
         return per
     fetch = counters(one("fetch/*counter_collection.csv"), "FETCH_SIZE")
     write = counters(one("write/*counter_collection.csv"), "WRITE_SIZE")
+    util_f = glob.glob(os.path.join(src, "util/*counter_collection.csv"))
+    util = {n: counters(util_f[0], n) for n in ("MfmaUtil", "VALUBusy", "LdsUtil", "LdsBankConflict")} \
+        if util_f else {}
     copy_f, copy_w = max(fetch["__amd_rocclr_copyBuffer"]), max(write["__amd_rocclr_copyBuffer"])
     sf, sw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
     steps = {}
@@ -455,7 +559,8 @@ def summarize(src: str, workload: str):
         if st and st != "copy":
             steps[st] = dict(symbol=sym, calls=c, avg_us=avg, pct=pct,
                              fetch_bytes=float(np.mean(fetch.get(sym, [0.0]))) * 1024 * sf,
-                             write_bytes=float(np.mean(write.get(sym, [0.0]))) * 1024 * sw)
+                             write_bytes=float(np.mean(write.get(sym, [0.0]))) * 1024 * sw,
+                             util={n: round(float(np.mean(v[sym])), 2) for n, v in util.items() if sym in v})
     dom = max(("expert_gate_up", "expert_down"), key=lambda k: steps.get(k, {}).get("avg_us", 0.0))
     cmds = profile_commands(workload)
     lines = [f"# {dom} on the {workload} workload (T={shape.T}, H{shape.H}/E{shape.E}/top{shape.K}, "
@@ -472,6 +577,16 @@ def summarize(src: str, workload: str):
               "| step | kernel | read MB | write MB |", "|---|---|---|---|"]
     for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
         lines.append(f"| {st} | `{e['symbol']}` | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} |")
+    if util:
+        lines += ["", "## Utilisation per launch (rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict)", "",
+                  "MfmaUtil = MFMA busy cycles / (GPU cycles x SIMDs) in %; VALUBusy = VALU instruction cycles "
+                  "per CU in %; LdsUtil = LDS busy cycles per CU in %; LdsBankConflict = conflict cycles per "
+                  "conflict-free LDS cycle.", "",
+                  "| step | MfmaUtil % | VALUBusy % | LdsUtil % | LdsBankConflict |", "|---|---|---|---|---|"]
+        for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
+            u = e["util"]
+            lines.append(f"| {st} | {u.get('MfmaUtil', float('nan')):.1f} | {u.get('VALUBusy', float('nan')):.1f} | "
+                         f"{u.get('LdsUtil', float('nan')):.1f} | {u.get('LdsBankConflict', float('nan')):.3f} |")
     os.makedirs(PROFILES, exist_ok=True)
     md = os.path.join(PROFILES, f"{dom}_{workload}_T{shape.T}.md")
     with open(md, "w") as fh:
@@ -483,7 +598,8 @@ def summarize(src: str, workload: str):
         rec = {}
     h = kernel_source_hash()
     rec[workload] = {st: dict(symbol=e["symbol"], fetch_bytes=round(e["fetch_bytes"]),
-                              write_bytes=round(e["write_bytes"]), avg_us=round(e["avg_us"], 2), source_sha256=h)
+                              write_bytes=round(e["write_bytes"]), avg_us=round(e["avg_us"], 2), util=e["util"],
+                              source_sha256=h)
                      for st, e in steps.items()}
     with open(TRAFFIC_RECORD, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
@@ -509,7 +625,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary T=8192 measurement")
+    ap.add_argument("--no-secondary", "--no-prefill", dest="no_secondary", action="store_true",
+                    help="skip the secondary workloads (prefill T=8192, skewed, MXFP4)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy and GEMM rates")
     ap.add_argument("--stack", type=int, default=0, metavar="L",
                     help="instead: decode (T=64) through L distinct layers, each with its own weights (L <= 32)")
     ap.add_argument("--dense", type=int, default=0, metavar="I",
@@ -554,10 +672,10 @@ def main():
         copy_probe(hip)
 
     shape = CONFIGS[args.workload]
+    measured = None if args.no_peaks else measured_peaks(hip)
     t0 = time.perf_counter()
-    base = CONFIGS["decode"] if shape.weight_format != "mxfp4" else shape
     log(f"drawing {shape.E} experts ({shape.weight_format}) ...")
-    experts = gen_experts(base if shape.weight_format != "mxfp4" else shape, seed=0)
+    experts = gen_experts(shape, seed=0)
     log(f"  {time.perf_counter() - t0:.1f} s; uploading")
     d = upload(shape, experts)
     torch.cuda.synchronize()
@@ -582,25 +700,59 @@ def main():
                    "T": shape.T, "hidden_size": shape.H, "num_experts": shape.E, "moe_intermediate_size": shape.I,
                    "n_group": shape.G, "topk_group": shape.TG, "num_experts_per_tok": shape.K,
                    "weights": shape.weight_format, "parallelism": "single GPU"},
-        "roofline": roofline(shape, r),
-        "layer": layer_summary(shape, r),
+        "roofline": roofline(shape, r, measured=measured),
+        "layer": layer_summary(shape, r, measured),
         "kernels_ms": {k: round(v, 4) for k, v in r["kernels"].items()},
         "kernels_ms_from": "forwards with an event after every kernel, outside the timed region",
         "event_ms_per_step": round(r["event_ms"], 4),
+        "measured_peaks": measured,
         "expert_bias_update": time_bias_update(shape, r["counts"], hip),
     }
-    if not args.no_prefill and shape.name == "decode":
-        p = CONFIGS["prefill"]
-        dp = upload(p, experts)
-        log(f"measuring prefill T={p.T}")
-        rp = measure(p, dp, max(5, args.steps // 3), 3, hip)
-        line["prefill"] = {"workload": f"prefill: T={p.T}, same layer", "value": round(p.T / (rp["wall_ms"] * 1e-3), 1),
-                           "unit": "tokens/s", "ms_per_step": round(rp["wall_ms"], 4), "roofline": roofline(p, rp),
-                           "layer": layer_summary(p, rp), "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
-        del dp
+    host = ("x_bits", "router_w_np", "bias_np")
+    checks = [(shape, {k: d[k] for k in host}, r["idx"])]
+    if not args.no_secondary and shape.name == "decode":
+        # the other workloads on the same layer: prefill (the metric's T=8192), skewed routing
+        # with the deep-layer clamp, and the routed experts in MXFP4 (quantised from the same
+        # bf16 draw, as the MXFP4 workload's generator does)
+        from synthetic import quantise_mxfp4
+        from concurrent.futures import ThreadPoolExecutor
+        line["secondary"] = {}
+        for name in ("prefill", "skewed", "mxfp4"):
+            p = CONFIGS[name]
+            ex = experts
+            if p.weight_format == "mxfp4":
+                log("quantising the experts to MXFP4 ...")
+                ex = {k + sfx: np.empty((p.E,) + experts[k].shape[1:2] + (experts[k].shape[2] // div,), np.uint8)
+                      for k in ("gate", "up", "down") for sfx, div in (("_q", 2), ("_s", 32))}
+
+                def q(e):
+                    for k in ("gate", "up", "down"):
+                        ex[k + "_q"][e], ex[k + "_s"][e] = quantise_mxfp4(experts[k][e])
+                with ThreadPoolExecutor(16) as pool:
+                    list(pool.map(q, range(p.E)))
+            dp = upload(p, ex)
+            log(f"measuring {name} T={p.T}")
+            rp = measure(p, dp, max(5, args.steps // 3), 3, hip)
+            line["secondary"][name] = {
+                "workload": f"{name}: T={p.T}, same layer" + (", clamp 4 / 7, clustered tokens, bias N(0,0.5)"
+                                                               if name == "skewed" else
+                                                               ", routed experts MXFP4" if name == "mxfp4" else ""),
+                "value": round(p.T / (rp["wall_ms"] * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(rp["wall_ms"], 4),
+                "dtype": "bf16" if p.weight_format == "bf16" else "mxfp4-w/bf16",
+                "roofline": roofline(p, rp, measured=measured), "layer": layer_summary(p, rp, measured),
+                "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
+            checks.append((p, {k: dp[k] for k in host}, rp["idx"]))
+            if p.weight_format == "mxfp4":
+                del ex
+            del dp
+            torch.cuda.empty_cache()
+        line["prefill"] = line["secondary"]["prefill"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(shape, d, experts, args.cpu_tokens)
+        # the oracle's routing of every measured step, beside the GPU's
+        line["routing_check"] = {c[0].name: routing_check(*c) for c in checks}
     print(json.dumps(line), flush=True)
 
 

@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions
@@ -58,6 +59,10 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's achievable-rate probes: a library of their own, outside libmoe's ABI
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, *FLAGS, "-shared", "-o", tmp, os.path.join(PKG, "probe", "peak_probe.hip")], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,92 @@
+// Achievable-rate probes for the benchmark: what this GPU sustains for a plain HBM read, a
+// plain copy and a loop of bf16 MFMAs, so that kernel figures can be set against measured
+// rates beside the nominal peaks.  Built as libmoe_probe.so, separate from libmoe's ABI; only
+// the benchmark loads it.  Every launch is bounded by its arguments (grid-stride loops over n
+// elements; a fixed number of MFMA iterations) and writes only the sink it is given.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr uint32_t NEVER = 0x9E3779B9u;  // a sink value the data never produces in practice
+
+// sum of n 16-byte elements, four loads in flight per lane; one word per workgroup is written
+// only if the xor of its data equals NEVER, which keeps every load live
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, size_t n, uint32_t* __restrict__ sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n; i += stride) acc ^= src[i];
+  const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == NEVER) sink[blockIdx.x] = r;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// `iters` rounds of 8 independent 16x16x32 bf16 MFMAs per wave (operands from the lane id,
+// so nothing folds); one float per workgroup is written only if the sum equals a value it
+// never takes in practice
+__global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* __restrict__ sink) {
+  const uint32_t l = threadIdx.x;
+  const u32x4 ab = {0x3F803F80u ^ (l & 7u), 0x3F003F00u ^ (l & 3u), 0x3E803E80u, 0x3F803F80u};
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ab);
+  floatx4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, (float)j};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// plain HBM read of n16 16-byte elements from src; sink: device, >= grid words
+int moe_probe_read(const void* src, size_t n16, void* sink, int grid, void* stream) {
+  if (!src || !sink || grid <= 0) return -1;
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
+                     (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// plain copy of n16 16-byte elements
+int moe_probe_copy(const void* src, void* dst, size_t n16, int grid, void* stream) {
+  if (!src || !dst || grid <= 0) return -1;
+  hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// grid workgroups of 4 waves, each wave 8 * iters bf16 MFMAs of 16x16x32 (16384 flops each);
+// sink: device, >= grid floats
+int moe_probe_mfma_bf16(int iters, int grid, void* sink, void* stream) {
+  if (!sink || grid <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_bf16_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, (float*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // extern "C"
