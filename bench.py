@@ -109,7 +109,7 @@ def upload(shape, experts, seed=0):
     sh = gen_shared(shape, seed)
     d["shared_np"] = sh
     shared = [dev(sh[k], True) for k in ("gate", "up", "down")]
-    if shape.weight_format == "mxfp4":
+    if shape.weight_format in ("mxfp4", "mxfp8"):
         w = moe.MoEExpertWeights(*[dev(experts[k]) for k in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")],
                                  *shared)
     else:
@@ -126,14 +126,22 @@ def cfg_for(shape):
                          num_shared_experts=shape.num_shared_experts, shared_intermediate_size=shape.I_s,
                          norm_topk_prob=int(shape.norm_topk_prob), routed_scaling_factor=shape.routed_scaling_factor,
                          swiglu_limit=shape.swiglu_limit, shared_swiglu_limit=shape.shared_swiglu_limit,
-                         expert_weight_format=moe.MOE_WEIGHTS_MXFP4 if shape.weight_format == "mxfp4"
-                         else moe.MOE_WEIGHTS_BF16)
+                         expert_weight_format={"bf16": moe.MOE_WEIGHTS_BF16, "mxfp4": moe.MOE_WEIGHTS_MXFP4,
+                                               "mxfp8": moe.MOE_WEIGHTS_MXFP8}[shape.weight_format],
+                         expert_act_format=moe.MOE_ACT_MXFP8 if shape.act_format == "mxfp8" else moe.MOE_ACT_BF16)
+
+
+def dtype_of(shape):
+    """Arithmetic types of the step: weights / activations of the routed experts' products."""
+    if shape.weight_format == "bf16":
+        return "bf16"
+    return f"{shape.weight_format}-w/{'mxfp8' if shape.act_format == 'mxfp8' else 'bf16'}-a"
 
 
 def expert_bytes(shape):
     """Bytes of one routed expert's weights (gate, up, down) in its storage format."""
     n = 3 * shape.H * shape.I
-    return n // 2 + n // 32 if shape.weight_format == "mxfp4" else 2 * n
+    return {"mxfp4": n // 2 + n // 32, "mxfp8": n + n // 32}.get(shape.weight_format, 2 * n)
 
 
 def measure(shape, d, steps, warmup, hip):
@@ -400,7 +408,7 @@ def measured_peaks(hip, nbytes=1 << 30, n=4096):
                 hip.record(e1, stream)
                 t = min(t, hip.elapsed_ms(e0, e1))
         return t
-    grids = (1024, 2048, 4096, 8192)
+    grids = (1024, 2048, 4096, 8192, 16384)
     t_read = best(lambda g: lib.moe_probe_read(V(a.data_ptr()), S(n16), V(sink.data_ptr()), I(g), V(stream)), grids)
     t_copy = best(lambda g: lib.moe_probe_copy(V(a.data_ptr()), V(b.data_ptr()), S(n16), I(g), V(stream)), grids)
     iters = 2000
@@ -462,8 +470,9 @@ def cpu_baseline(shape, d, experts, max_tokens):
     x = oracle.bf16_to_f64(d["x_bits"][:T])
 
     def get(e):
-        if shape.weight_format == "mxfp4":
-            return tuple(oracle.mxfp4_dequant(experts[k + "_q"][e], experts[k + "_s"][e]) for k in ("gate", "up", "down"))
+        if shape.weight_format in ("mxfp4", "mxfp8"):
+            dq = oracle.mxfp4_dequant if shape.weight_format == "mxfp4" else oracle.mxfp8_dequant
+            return tuple(dq(experts[k + "_q"][e], experts[k + "_s"][e]) for k in ("gate", "up", "down"))
         return tuple(oracle.bf16_to_f64(experts[k][e]) for k in ("gate", "up", "down"))
     sh = tuple(oracle.bf16_to_f64(d["shared_np"][k]) for k in ("gate", "up", "down"))
     # the whole sample again until about 10 s of CPU work have been timed
@@ -473,7 +482,8 @@ def cpu_baseline(shape, d, experts, max_tokens):
         oracle.moe_layer(x, d["router_w_np"], d["bias_np"], get, sh, n_group=shape.G, topk_group=shape.TG,
                          top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
                          norm_topk_prob=shape.norm_topk_prob, swiglu_limit=shape.swiglu_limit,
-                         shared_swiglu_limit=shape.shared_swiglu_limit)
+                         shared_swiglu_limit=shape.shared_swiglu_limit,
+                         act_quant="mxfp8" if shape.act_format == "mxfp8" else "none")
         dt += time.perf_counter() - t0
         passes += 1
     try:
@@ -623,7 +633,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed", "mxfp4"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skewed", "mxfp4", "mxfp8", "mxfp4_a8", "mxfp8_a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", "--no-prefill", dest="no_secondary", action="store_true",
                     help="skip the secondary workloads (prefill T=8192, skewed, MXFP4)")
@@ -693,7 +704,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if shape.weight_format == "bf16" else "mxfp4-w/bf16",
+        "dtype": dtype_of(shape),
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
         "config": {"workload": f"{shape.name}: T={shape.T}, hidden {shape.H}, {shape.E} experts (I={shape.I}) "
                                f"in {shape.G} groups, top-{shape.TG} groups, top-{shape.K}, 1 shared expert",
@@ -739,7 +750,7 @@ def main():
                                                                ", routed experts MXFP4" if name == "mxfp4" else ""),
                 "value": round(p.T / (rp["wall_ms"] * 1e-3), 1), "unit": "tokens/s",
                 "ms_per_step": round(rp["wall_ms"], 4),
-                "dtype": "bf16" if p.weight_format == "bf16" else "mxfp4-w/bf16",
+                "dtype": dtype_of(p),
                 "roofline": roofline(p, rp, measured=measured), "layer": layer_summary(p, rp, measured),
                 "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
             checks.append((p, {k: dp[k] for k in host}, rp["idx"]))

@@ -56,7 +56,16 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed; moe_last_error() has the HIP text */
 } moe_status_t;
 
-typedef enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_MXFP4 = 1 } moe_weight_format_t;
+typedef enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_MXFP4 = 1, MOE_WEIGHTS_MXFP8 = 2 } moe_weight_format_t;
+
+/* Activations of the routed experts' two matrix products.  MOE_ACT_BF16: x as given (bf16)
+ * and h kept as two bf16 planes (about 16 significand bits).  MOE_ACT_MXFP8 (MXFP4 or MXFP8
+ * weights only): x and h rounded to MXFP8 -- E4M3 values with one e8m0 scale per 32
+ * consecutive values along the reduction (OCP MX v1.0: scale = 2^(floor(log2 amax) - 8),
+ * round to nearest even, saturate at 448) -- and multiplied by gfx950's scaled MFMA; the
+ * shared expert keeps bf16 activations.  The hybrid-attention page (table 模型一览) lists the
+ * quantised model as "FP8 + MXFP4". */
+typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP8 = 1 } moe_act_format_t;
 
 /* Layer configuration.  Field names follow the model's config.json text_config as the
  * routing walk-through page quotes them (sections 二, 三.2 and 四). */
@@ -74,6 +83,7 @@ typedef struct {
   float swiglu_limit;               /* > 0: clamp routed activations to [-limit, limit] */
   float shared_swiglu_limit;        /* > 0: clamp shared-expert activations */
   int32_t expert_weight_format;     /* moe_weight_format_t of the routed experts */
+  int32_t expert_act_format;        /* moe_act_format_t of the routed experts (0: bf16) */
 } moe_config_t;
 
 /* Expert weights, all device pointers, PyTorch [out_features, in_features] layout.
@@ -82,6 +92,9 @@ typedef struct {
  *                      codes per byte (low nibble = even k, nibble = sign<<3 | code),
  *                      gate_scale/up_scale [E,I,H/32], down_scale [E,H,I/32] e8m0
  *                      bytes (value = e2m1 * 2^(scale-127), one scale per 32 k).
+ *   MOE_WEIGHTS_MXFP8: gate [E,I,H], up [E,I,H], down [E,H,I] uint8 E4M3 codes (OCP FP8:
+ *                      sign<<7 | exponent (bias 7)<<3 | mantissa; 0x7f/0xff NaN, never
+ *                      given), scales as for MXFP4 (value = e4m3 * 2^(scale-127)).
  *   Shared expert (bf16, required when S == 1, else ignored):
  *                      shared_gate [I,H], shared_up [I,H], shared_down [H,I]. */
 typedef struct {
@@ -181,6 +194,18 @@ moe_status_t moe_dense_ffn_workspace_size(int32_t hidden_size, int32_t intermedi
 moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float swiglu_limit, int64_t T,
                            const void* x, const void* gate, const void* up, const void* down, void* out,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP8 rounding of bf16 activations, the step the MOE_ACT_MXFP8 path applies to x before
+ * the routed experts' gate/up products (the same device code rounds h in the gate/up
+ * epilogue): for each block of 32 consecutive values of a row, scale = 2^X with
+ * X = floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an all-zero block), and each
+ * v / 2^X rounded to the nearest E4M3 value, ties to even, saturated at 448 (OCP MX v1.0).
+ *   x       device bf16 [rows, cols]; cols a positive multiple of 32
+ *   codes   device uint8 [rows, cols]     E4M3 codes (16-byte aligned)
+ *   scales  device uint8 [rows, cols/32]  e8m0 bytes X + 127
+ * Enqueued on `stream`; rows = 0 is a no-op. */
+moe_status_t moe_quantise_mxfp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                                void* stream);
 
 /* Expert-bias update, the step after the layer in training (routing walk-through page,
  * section 三.3: every routed expert's selection bias is lowered when it is busy and raised

@@ -4,6 +4,7 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 benchmark's CPU-baseline leg.  The HIP library never calls it and shares no code
 with it.
 """
-from .moe_oracle import (Dispatch, Routing, bf16_to_f64, dispatch, expert_forward,  # noqa: F401
-                         expert_hidden, moe_layer, mxfp4_dequant, route, router_logits, swiglu,
+from .moe_oracle import (E4M3_MAX, Dispatch, Routing, act_mxfp8, bf16_to_f64, dispatch,  # noqa: F401
+                         e4m3_value, expert_forward, expert_hidden, moe_layer, mxfp4_dequant,
+                         mxfp8_dequant, mxfp8_quantise, route, router_logits, swiglu,
                          update_expert_bias)

@@ -72,6 +72,71 @@ def mxfp4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return val * np.repeat(sc, 32, axis=1)
 
 
+# FP8 E4M3 (OCP 8-bit floating point, as used by the OCP MX v1.0 MXFP8 format): sign bit 7,
+# exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); the
+# all-ones exponent with all-ones mantissa is NaN and there are no infinities, so the largest
+# finite magnitude is 1.75 * 2^8 = 448.
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest normal value
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    """E4M3 code (uint8) -> float64 value (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(code, dtype=np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 (E4M3 elements, one e8m0 scale per 32 consecutive values of the last axis) ->
+    float64: value = e4m3 * 2^(scale - 127)."""
+    v = e4m3_value(codes)
+    sc = np.exp2(np.asarray(scales, dtype=np.float64) - 127.0)
+    return v * np.repeat(sc, 32, axis=-1)
+
+
+# the 127 non-negative finite E4M3 values, indexed by their code (ascending)
+_E4M3_GRID = e4m3_value(np.arange(127))
+
+
+def mxfp8_quantise(a: np.ndarray):
+    """float64 [..., K] -> (E4M3 codes uint8 [..., K], e8m0 scales uint8 [..., K/32]).
+
+    The OCP MX v1.0 conversion for E4M3 elements, per block of 32 consecutive values of the
+    last axis: shared exponent X = floor(log2(max |v|)) - 8 (8 = the exponent of E4M3's
+    largest normal value), clamped to the e8m0 range [-127, 127] (-127 for an all-zero
+    block); each v / 2^X rounded to the nearest E4M3 value, ties to the even code, and
+    magnitudes beyond 448 saturated to 448."""
+    a = np.asarray(a, dtype=np.float64)
+    K = a.shape[-1]
+    assert K % 32 == 0
+    blk = a.reshape(a.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    mag = np.abs(blk) / np.exp2(X.astype(np.float64))[..., None]
+    # nearest grid value: i = number of grid values <= mag, so mag lies in [grid[i-1], grid[i])
+    i = np.searchsorted(_E4M3_GRID, mag, side="right")
+    lo = np.clip(i - 1, 0, 126)
+    hi = np.clip(i, 0, 126)
+    dlo, dhi = mag - _E4M3_GRID[lo], _E4M3_GRID[hi] - mag
+    code = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(mag >= E4M3_MAX, 126, code)          # saturate (126 is 448)
+    neg = (blk < 0) & (code != 0)
+    codes = (code | (neg.astype(np.int64) << 7)).astype(np.uint8).reshape(a.shape)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def act_mxfp8(a: np.ndarray) -> np.ndarray:
+    """The values an MXFP8 matrix product sees for the activations a (last axis = the
+    reduction axis): a quantised to MXFP8 and decoded again."""
+    return mxfp8_dequant(*mxfp8_quantise(a))
+
+
 # ----------------------------------------------------------------------------------
 # routing ([R] sections 三.1-三.3, 四)
 # ----------------------------------------------------------------------------------
@@ -212,9 +277,18 @@ def expert_hidden(xrows, gate, up, limit=0.0):
     return swiglu(xrows @ gate.T, xrows @ up.T, limit)
 
 
-def expert_forward(xrows, gate, up, down, limit=0.0):
-    """One SwiGLU expert ([R] 二: three matrices gate / up / down): [n,H] -> [n,H]."""
-    return expert_hidden(xrows, gate, up, limit) @ down.T
+def expert_forward(xrows, gate, up, down, limit=0.0, act_quant: str = "none"):
+    """One SwiGLU expert ([R] 二: three matrices gate / up / down): [n,H] -> [n,H].
+
+    act_quant="mxfp8": the expert's two matrix products take MXFP8 activations (the
+    8-bit-activation reading of [Q] table 模型一览's "FP8 + MXFP4"): x is rounded to MXFP8
+    along H before gate/up, and h (after SwiGLU and the clamp) along I before down."""
+    if act_quant == "none":
+        return expert_hidden(xrows, gate, up, limit) @ down.T
+    if act_quant != "mxfp8":
+        raise ValueError(act_quant)
+    h = expert_hidden(act_mxfp8(xrows), gate, up, limit)
+    return act_mxfp8(h) @ down.T
 
 
 ExpertGetter = Callable[[int], tuple]   # e -> (gate [I,H], up [I,H], down [H,I]) float64
@@ -224,10 +298,11 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray],
               get_expert: ExpertGetter, shared: Optional[tuple], *, n_group: int,
               topk_group: int, top_k: int, routed_scaling_factor: float = 2.5,
               norm_topk_prob: bool = True, swiglu_limit: float = 0.0,
-              shared_swiglu_limit: float = 0.0, decision: str = "fp32"):
+              shared_swiglu_limit: float = 0.0, decision: str = "fp32", act_quant: str = "none"):
     """Forward of the whole block: route, run each chosen expert on its tokens, sum the
     weighted outputs per token in ascending expert order, add the shared expert.
-    Returns (out [T,H] float64, Routing)."""
+    act_quant applies to the routed experts only (see expert_forward); the shared expert
+    always takes the exact activations.  Returns (out [T,H] float64, Routing)."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     r = route(router_logits(x, router_w), bias, n_group, topk_group, top_k,
@@ -236,7 +311,7 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray],
     for e in np.unique(r.topk_idx):
         tok, slot = np.nonzero(r.topk_idx == e)
         g, u, d = get_expert(int(e))
-        y = expert_forward(x[tok], g, u, d, swiglu_limit)
+        y = expert_forward(x[tok], g, u, d, swiglu_limit, act_quant)
         out[tok] += r.topk_w[tok, slot][:, None] * y
     if shared is not None:
         out += expert_forward(x, *shared, shared_swiglu_limit)

@@ -18,16 +18,20 @@ from typing import Optional
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
            "moe_forward_timed", "moe_update_expert_bias", "moe_dense_ffn_workspace_size", "moe_dense_ffn",
-           "moe_forward_noalloc", "moe_status_string",
-           "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "EXPORTED_SYMBOLS"]
+           "moe_forward_noalloc", "moe_quantise_mxfp8", "moe_status_string",
+           "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "MOE_WEIGHTS_MXFP8", "MOE_ACT_BF16", "MOE_ACT_MXFP8",
+           "EXPORTED_SYMBOLS"]
 
 MOE_WEIGHTS_BF16 = 0
 MOE_WEIGHTS_MXFP4 = 1
+MOE_WEIGHTS_MXFP8 = 2
+MOE_ACT_BF16 = 0
+MOE_ACT_MXFP8 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_update_expert_bias",
-                    "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_forward_noalloc", "moe_status_string",
-                    "moe_last_error")
+                    "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_forward_noalloc", "moe_quantise_mxfp8",
+                    "moe_status_string", "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -44,7 +48,7 @@ class MoEConfig(ctypes.Structure):
                 ("num_shared_experts", ctypes.c_int32), ("shared_intermediate_size", ctypes.c_int32),
                 ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
                 ("swiglu_limit", ctypes.c_float), ("shared_swiglu_limit", ctypes.c_float),
-                ("expert_weight_format", ctypes.c_int32)]
+                ("expert_weight_format", ctypes.c_int32), ("expert_act_format", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -95,6 +99,7 @@ def load_library():
         "moe_dense_ffn_workspace_size": [ctypes.c_int32, ctypes.c_int32, I64, ctypes.POINTER(SZ)],
         "moe_dense_ffn": [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I64, P, P, P, P, P, P, SZ, P],
         "moe_forward_noalloc": [C, I64, P, P, P, W, P, P, P, P, P],
+        "moe_quantise_mxfp8": [P, I64, ctypes.c_int32, P, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -227,3 +232,9 @@ def moe_forward_noalloc(cfg, T, x, router_w, expert_bias, weights: MoEExpertWeig
     _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
                                               ctypes.byref(weights.struct), _ptr(out), _ptr(topk_idx_out),
                                               _ptr(topk_w_out), _ptr(expert_counts_out), _stream(stream)))
+
+
+def moe_quantise_mxfp8(x, rows, cols, codes, scales, stream=None):
+    """bf16 [rows, cols] -> MXFP8 E4M3 codes [rows, cols] and e8m0 scales [rows, cols/32] (the
+    rounding the MXFP8-activation path applies to x)."""
+    _check(load_library().moe_quantise_mxfp8(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))

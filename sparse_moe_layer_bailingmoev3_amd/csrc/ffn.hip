@@ -3,7 +3,8 @@
 // Each expert is a SwiGLU FFN of three matrices, gate and up (hidden -> intermediate) and
 // down (intermediate -> hidden) (Ling-3.0-flash-VL routing walk-through page, lqnn.cn,
 // section 二); activations may be clamped to +-limit (section 四, expert_swiglu_limit_list);
-// routed-expert weights may be MXFP4 (hybrid-attention page, lpnh.cn, table 模型一览).
+// routed-expert weights may be MXFP4 or MXFP8 (hybrid-attention page, lpnh.cn, table 模型一览:
+// "FP8 + MXFP4").
 //
 // Work unit (one workgroup): expert e, a tile of up to 16*MF consecutive sorted positions
 // of that expert, and a block of NW*RF*16 weight rows.  Design for gfx950:
@@ -21,8 +22,9 @@
 //     the activation h is stored as two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
 //     and the down projection runs one MFMA per plane, so h keeps ~16 significand bits
 //     through the down GEMM; the down projection writes fp32 expert outputs;
-//   * MXFP4 weights (KS = 128: one 16-byte load = 32 codes = one scale block per lane) are
-//     decoded exactly to bf16 in registers by the gfx950 scaled fp4 -> bf16 conversion;
+//   * MXFP4 weights (KS = 128: one 16-byte load = 32 codes = one scale block per lane) and
+//     MXFP8 weights (two 16-byte loads for the same 32 values) are decoded exactly to bf16 in
+//     registers by gfx950's scaled fp4 / fp8 -> bf16 conversions;
 //   * the work list (tiles per expert) lives on the device; consecutive work ids are placed
 //     on the same XCD so the row blocks of one tile share its token rows in that XCD's L2.
 #include "moe_common.h"
@@ -42,8 +44,8 @@ struct FfnArgs {
   const int32_t* tile_prefix;   // [E+2] tiles of all experts before e
   const void* w0;               // routed gate (gate/up) or down
   const void* w1;               // routed up (gate/up)
-  const uint8_t* s0;            // MXFP4 scales of w0
-  const uint8_t* s1;            // MXFP4 scales of w1
+  const uint8_t* s0;            // MX (block-format) scales of w0
+  const uint8_t* s1;            // MX scales of w1
   const void* sw0;              // shared expert gate or down
   const void* sw1;              // shared expert up
   void* out;                    // gate/up: h hi plane bf16 [P,N]; down: y fp32 [P,N]
@@ -61,7 +63,16 @@ struct FfnArgs {
   int ksplit;                   // workgroups splitting the reduction (down of a dense FFN; else 1)
   float* part;                  // ksplit > 1: fp32 partial sums [ksplit,T,N], added in order later
   float limit, shared_limit;
+  // MXFP8 activations of the routed experts (the scaled-MFMA path): codes and e8m0 scales of
+  // the token operand (gate/up: x [T,K] and [T,K/32]; down: h [P,K] and [P,K/32]) and, for
+  // gate/up, of the h it writes ([P,N] and [P,N/32])
+  const uint8_t* aq;
+  const uint8_t* as;
+  uint8_t* oq;
+  uint8_t* os;
 };
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -73,6 +84,18 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t v, float scale) {
   o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1));
   o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2));
   o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3));
+  return o;
+}
+
+// 8 E4M3 codes (two words, low byte first) times a power of two -> 8 bf16 (exact: every E4M3
+// value times 2^(s-127) within the e8m0 range is a bf16).  gfx950 converts two codes (one
+// 16-bit half of a word) per instruction.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t v0, uint32_t v1, float scale) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v0, scale, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v0, scale, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v1, scale, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v1, scale, true));
   return o;
 }
 
@@ -94,7 +117,7 @@ struct TStage {
 // One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
 // tile) are issued while step s computes, all in one batch, so that waiting for the token
 // tile of the next step (loads complete in issue order) never waits for younger weights.
-template <int NW, int RF, int MF, int D, int MODE, int KS, bool FP4, bool PADDED>
+template <int NW, int RF, int MF, int D, int MODE, int KS, int WF, bool PADDED>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                          int ksp, uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
@@ -106,7 +129,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
   constexpr int CHUNKS = BM * KS / 8;  // 16-byte pieces of one token plane per step
   constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
   constexpr int ROWS = NW * RF * 16;
-  constexpr int WREGS = FP4 ? 1 : SUB;
+  constexpr bool MX = WF != FMT_BF16;       // block-format weights (MXFP4 or MXFP8), KS = 128
+  constexpr bool FP4 = WF == FMT_MXFP4;
+  constexpr int WREGS = MX ? (FP4 ? 1 : 2) : SUB;  // 16-byte weight registers per (matrix, row block) and step
+  static_assert(!MX || KS == 128, "MX weights take 128-value steps");
   // PADDED, the loop form (each measured fastest for its kernels): tiles of 64+ tokens and
   // the MXFP4 kernel issue every load unconditionally; 16- and 32-token tiles do not
 
@@ -144,9 +170,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
   }
 
   // weight rows of this lane.  bf16: sub-step s of a step reads k = 32s + 8q .. +7, so
-  // one load instruction covers 64 contiguous bytes of each of the 16 rows.  MXFP4: lane
-  // group q owns the 32-value block q of the step (16 bytes of codes, one scale byte) and
-  // sub-step s uses its codes 8s .. 8s+7.
+  // one load instruction covers 64 contiguous bytes of each of the 16 rows.  MXFP4 / MXFP8:
+  // lane group q owns the 32-value block q of the step (16 / 32 bytes of codes, one scale
+  // byte) and sub-step s uses its codes 8s .. 8s+7.
   const int nbase = rb0 * ROWS + wave * RF * 16;
   const uint16_t* wp[NMAT][RF];
   const uint8_t* wq[NMAT][RF];
@@ -156,10 +182,11 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
       const size_t row = (size_t)(nbase + f * 16 + r16);
-      if constexpr (FP4) {
-        const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / 2);
+      if constexpr (MX) {
+        constexpr int VPB = FP4 ? 2 : 1;  // values per byte
+        const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / VPB);
         const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
-        wq[m][f] = base + row * (K / 2) + k0 / 2 + q * (KS / 8);
+        wq[m][f] = base + row * (K / VPB) + k0 / VPB + q * (KS / 4 / VPB);
         wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + q * (KS / 128);
         wp[m][f] = nullptr;
       } else {
@@ -209,8 +236,11 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
-        if constexpr (FP4) {
-          st.w[m][f][0] = *(const u32x4*)(wq[m][f] + (size_t)rbi * ROWS * (K / 2) + (size_t)ks * (KS / 2));
+        if constexpr (MX) {
+          constexpr int VPB = FP4 ? 2 : 1;
+          const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (KS / VPB);
+#pragma unroll
+          for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + 16 * r);
           st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32)];
         } else {
 #pragma unroll
@@ -219,18 +249,27 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         }
       }
   };
+  // the 8 weights of sub-step s (codes 8s .. 8s+7 of the lane's 32-value block) as bf16
+  auto decode_mx = [&](const WStage<NMAT, RF, WREGS>& st, int m, int f, int s) -> u32x4 {
+    const float sc = e8m0_to_f32(st.sc[m][f]);
+    if constexpr (FP4) {
+      return fp4x8_to_bf16x8(st.w[m][f][0][s], sc);
+    } else {
+      return fp8x8_to_bf16x8(st.w[m][f][s >> 1][(2 * s) & 3], st.w[m][f][s >> 1][(2 * s + 1) & 3], sc);
+    }
+  };
   auto compute_at_use = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
     const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      const int col = FP4 ? q * 32 + s * 8 : s * 32 + q * 8;
+      const int col = MX ? q * 32 + s * 8 : s * 32 + q * 8;
       u32x4 wf[NMAT][RF];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-          if constexpr (FP4) {
-            wf[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+          if constexpr (MX) {
+            wf[m][f] = decode_mx(st, m, f, s);
           } else {
             wf[m][f] = st.w[m][f][s];
           }
@@ -260,21 +299,21 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
     const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
     u32x4 tf[2][NTP][MF];
     auto read_frags = [&](u32x4 (&t)[NTP][MF], int s) {
-      const int col = FP4 ? q * 32 + s * 8 : s * 32 + q * 8;
+      const int col = MX ? q * 32 + s * 8 : s * 32 + q * 8;
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int p = 0; p < NTP; ++p) t[p][mf] = *(const u32x4*)(L + p * BM * LROW + mf * 16 * LROW + col);
     };
-    // MXFP4: the weights of sub-step s + 1 are also decoded while sub-step s multiplies
+    // MX weights: those of sub-step s + 1 are also decoded while sub-step s multiplies
     u32x4 wf[2][NMAT][RF];
     auto weights = [&](u32x4 (&w)[NMAT][RF], int s) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-          if constexpr (FP4) {
-            w[m][f] = fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
+          if constexpr (MX) {
+            w[m][f] = decode_mx(st, m, f, s);
           } else {
             w[m][f] = st.w[m][f][s];
           }
@@ -393,9 +432,287 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
   }
 }
 
-template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS>
+// One work unit with MXFP8 activations (routed experts with MXFP4 or MXFP8 weights).  The
+// token operand -- x rows gathered for gate/up, h rows for down -- is E4M3 codes with one e8m0
+// scale per 32 values, staged in double-buffered LDS with its scales; each 16x16x128 product
+// is one scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), which applies both operands' block
+// scales, so no decode instruction runs.  Operand layout of that instruction (measured on
+// gfx950 with one-hot operands): lane (r16, q) gives the scale of row r16's 32-value block q
+// (byte 0 of its scale register); an E2M1 operand holds that block's 32 values in the lane
+// (low nibble first); an E4M3 operand holds k = 16q .. 16q+15 in its first 16 bytes and
+// k = 64+16q .. 64+16q+15 in its last 16.  The gate/up epilogue rounds h to
+// MXFP8 along the intermediate dimension: a block of 32 rows is two 16-row fragments of one
+// wave, its maximum taken over the four lane groups; down then reads the 8-bit h.
+template <int NW, int RF, int MF, int D, int MODE, int WF>
+__device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
+                                            uint8_t* lds) {
+  constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+  constexpr int BM = MF * 16;
+  constexpr int KS = 128;
+  constexpr int LROW = KS + 16;            // bytes per token row in LDS (16-byte pad)
+  constexpr int NTH = NW * 64;
+  constexpr int CHUNKS = BM * KS / 16;     // 16-byte pieces of the token codes per step
+  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
+  constexpr int ROWS = NW * RF * 16;
+  constexpr bool FP4 = WF == FMT_MXFP4;
+  constexpr int WREGS = FP4 ? 1 : 2;
+  constexpr int VPB = FP4 ? 2 : 1;         // weight values per byte
+  constexpr int AFMT = FP4 ? 4 : 0;        // scaled-MFMA operand format: 4 = E2M1, 0 = E4M3
+  static_assert(MODE == MODE_DOWN || RF % 2 == 0, "h is rounded in 32-row blocks: two fragments per wave");
+  static_assert(BM <= NTH, "one thread per token row loads its scales");
+  uint8_t* tcode = lds;                                 // [2][BM][LROW]
+  uint32_t* tscale = (uint32_t*)(lds + 2 * BM * LROW);  // [2][BM]: the step's 4 scale bytes of a row
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N;
+  const int nsteps = K / KS;
+  const int total_steps = nsteps * nrb_here;
+
+  // token codes: per-thread 16-byte pieces (row, col); a piece past the tile or of a position
+  // without a token reads a valid row and is stored as zeros (code 0 is +0 at any scale)
+  const uint8_t* tsrc[CPT];
+  bool tvalid[CPT];
+  int tdst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * NTH;
+    const int row = c < CHUNKS ? c / (KS / 16) : 0, col = (c % (KS / 16)) * 16;
+    tdst[i] = c < CHUNKS ? row * LROW + col : -1;
+    bool ok = c < CHUNKS && row < nrows;
+    const int prow = row < nrows ? row : 0;
+    if (MODE == MODE_GATEUP) {
+      const int tok = a.sorted_token[pos0 + prow];
+      ok = ok && (unsigned)tok < (unsigned)a.T;
+      tsrc[i] = a.aq + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + col;
+    } else {
+      tsrc[i] = a.aq + (size_t)(pos0 + prow) * K + col;
+    }
+    tvalid[i] = ok;
+  }
+  // token scales: thread tid < BM keeps those of row tid (the others read row 0's and store nothing)
+  const uint32_t* ssrc;
+  bool svalid;
+  {
+    const int row = tid < BM ? tid : 0;
+    const int prow = row < nrows ? row : 0;
+    bool ok = tid < BM && row < nrows;
+    if (MODE == MODE_GATEUP) {
+      const int tok = a.sorted_token[pos0 + prow];
+      ok = ok && (unsigned)tok < (unsigned)a.T;
+      ssrc = (const uint32_t*)(a.as + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * (K / 32));
+    } else {
+      ssrc = (const uint32_t*)(a.as + (size_t)(pos0 + prow) * (K / 32));
+    }
+    svalid = ok;
+  }
+
+  // weights: lane group q gives the scale of block q; E2M1 codes: block q's 16 bytes; E4M3
+  // codes: bytes 16q .. 16q+15 and 64+16q .. 64+16q+15 of the step (the instruction's layout)
+  const int nbase = rb0 * ROWS + wave * RF * 16;
+  const uint8_t* wq[NMAT][RF];
+  const uint8_t* wsc[NMAT][RF];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      const size_t row = (size_t)(nbase + f * 16 + r16);
+      const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / VPB);
+      const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
+      wq[m][f] = base + row * (K / VPB) + q * 16;
+      wsc[m][f] = sbase + row * (K / 32) + q;
+    }
+
+  struct WSt {
+    u32x4 w[NMAT][RF][WREGS];
+    uint32_t sc[NMAT][RF];
+  };
+  struct TSt {
+    u32x4 t[CPT];
+    uint32_t s;
+  };
+  floatx4 acc[NMAT][RF][MF];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // every step issues the same loads; past the last step they repeat its addresses into a
+  // ring slot that is not read again
+  auto load_t = [&](TSt& ts, int step) {
+    const int ks = min(step, total_steps - 1) % nsteps;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) ts.t[i] = *(const u32x4*)(tsrc[i] + ks * KS);
+    ts.s = ssrc[ks];
+  };
+  auto store_t = [&](const TSt& ts, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (tdst[i] >= 0) *(u32x4*)(tcode + buf * BM * LROW + tdst[i]) = tvalid[i] ? ts.t[i] : u32x4{0u, 0u, 0u, 0u};
+    if (tid < BM) tscale[buf * BM + tid] = svalid ? ts.s : 0x7F7F7F7Fu;  // scale 1 for zero rows
+  };
+  auto load_w = [&](WSt& st, int step) {
+    step = min(step, total_steps - 1);
+    const int rbi = step / nsteps, ks = step - rbi * nsteps;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (KS / VPB);
+#pragma unroll
+        for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + 64 * r);
+        st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32)];
+      }
+  };
+  // the token fragment of mf: row r16's codes 16q .. 16q+15 and 64+16q .. 64+16q+15, and the
+  // scale of its block q
+  auto bfrag = [&](int buf, int mf) {
+    const uint8_t* L = tcode + buf * BM * LROW + (mf * 16 + r16) * LROW + q * 16;
+    const u32x4 lo = *(const u32x4*)L, hi = *(const u32x4*)(L + 64);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto bscale = [&](int buf, int mf) { return (int)((tscale[buf * BM + mf * 16 + r16] >> (8 * q)) & 0xFFu); };
+  auto compute = [&](const WSt& st, int buf) {
+    i32x8 af[NMAT][RF];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        const u32x4 w0 = st.w[m][f][0];
+        const u32x4 w1 = FP4 ? u32x4{0u, 0u, 0u, 0u} : st.w[m][f][WREGS - 1];
+        af[m][f] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+      }
+    i32x8 bf[2];
+    int bs[2];
+    bf[0] = bfrag(buf, 0);
+    bs[0] = bscale(buf, 0);
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      if (mf + 1 < MF) {  // the next fragment's LDS reads overlap this one's MFMAs
+        bf[(mf + 1) & 1] = bfrag(buf, mf + 1);
+        bs[(mf + 1) & 1] = bscale(buf, mf + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+          acc[m][f][mf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[m][f], bf[mf & 1], acc[m][f][mf], AFMT, 0, 0, (int)st.sc[m][f], 0, bs[mf & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // lane holds token r16 of each fragment and rows 4q .. 4q+3 of each 16-row block
+  auto epilogue = [&](int rbi) {
+    const int ncol0 = nbase + rbi * ROWS;
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      const int j = mf * 16 + r16;
+      const bool keep = j < nrows;
+      if constexpr (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int fp = 0; fp < RF / 2; ++fp) {
+          float h[8];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float g = acc[0][2 * fp + hf][mf][r], u = acc[1][2 * fp + hf][mf][r];
+              float v = g / (1.0f + __expf(-g)) * u;
+              if (a.limit > 0.f) v = fminf(fmaxf(v, -a.limit), a.limit);
+              h[4 * hf + r] = v;
+            }
+          float am = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(h[i]));
+          am = fmaxf(am, __shfl_xor(am, 16, WAVE));
+          am = fmaxf(am, __shfl_xor(am, 32, WAVE));
+          const int sb = mx8_scale_byte(am), X = sb - 127;
+          const uint32_t c0 = mx8_pack4(h[0], h[1], h[2], h[3], X);
+          const uint32_t c1 = mx8_pack4(h[4], h[5], h[6], h[7], X);
+          if (keep) {
+            uint8_t* dst = a.oq + (size_t)(pos0 + j) * N + ncol0 + 32 * fp + 4 * q;
+            *(uint32_t*)dst = c0;
+            *(uint32_t*)(dst + 16) = c1;
+            if (q == 0) a.os[(size_t)(pos0 + j) * (N / 32) + (ncol0 + 32 * fp) / 32] = (uint8_t)sb;
+          }
+        }
+      } else {
+        if (keep) {
+#pragma unroll
+          for (int f = 0; f < RF; ++f)
+            *(floatx4*)((float*)a.out + (size_t)(pos0 + j) * N + ncol0 + f * 16 + 4 * q) = acc[0][f][mf];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[m][f][mf] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  WSt ws[D];
+  TSt ts[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_t(ts[j], j);
+    load_w(ws[j], j);
+  }
+  store_t(ts[0], 0);
+  block_sync_lds();
+  const int padded_steps = (total_steps + D - 1) / D * D;
+  for (int s0 = 0; s0 < padded_steps; s0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int st = s0 + j;
+      const bool real = st < total_steps;
+      if (real && st + 1 < total_steps) store_t(ts[(j + 1) % D], (st + 1) & 1);
+      if (real) compute(ws[j], st & 1);
+      load_t(ts[j], st + D);
+      load_w(ws[j], st + D);
+      if (real && (st + 1) % nsteps == 0) epilogue(st / nsteps);
+      block_sync_lds();
+    }
+  }
+}
+
+// x [rows, cols] bf16 -> MXFP8 codes [rows, cols] and e8m0 scales [rows, cols/32]: one 32-value
+// block per thread (64 bytes read, 33 written)
+__global__ __launch_bounds__(256) void mx8_quant_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x4* src = (const u32x4*)(x + i * 32);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 w = src[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * j + 2 * k] = __uint_as_float(w[k] << 16);
+      v[8 * j + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(v[j]));
+  const int sb = mx8_scale_byte(am), X = sb - 127;
+  u32x4 c[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j >> 2][j & 3] = mx8_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
+  ((u32x4*)(codes + i * 32))[0] = c[0];
+  ((u32x4*)(codes + i * 32))[1] = c[1];
+  scales[i] = (uint8_t)sb;
+}
+
+template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS, int ACT>
 __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
-  constexpr bool PADDED = FMT == FMT_MXFP4 || MF >= 4;
+  constexpr bool PADDED = FMT != FMT_BF16 || MF >= 4;
   constexpr int BM = MF * 16;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
   __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 16)];
@@ -431,13 +748,18 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int e = info.x, m0 = sub * BM;
   if (m0 >= info.z) return;
   const int nrows = min(BM, info.z - m0);
-  if constexpr (FMT == FMT_MXFP4) {
-    if (e < a.E) {
-      ffn_tile<NW, RF, MF, D, MODE, KS, true, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
+  if constexpr (FMT != FMT_BF16 && ACT == ACT_MXFP8) {
+    if (e < a.E) {  // routed experts: MXFP8 activations on the scaled MFMA
+      ffn_tile_a8<NW, RF, MF, D, MODE, FMT>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
+      return;
+    }
+  } else if constexpr (FMT != FMT_BF16) {
+    if (e < a.E) {  // routed experts in the block format; the shared expert is bf16
+      ffn_tile<NW, RF, MF, D, MODE, KS, FMT, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
       return;
     }
   }
-  ffn_tile<NW, RF, MF, D, MODE, KS, false, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
+  ffn_tile<NW, RF, MF, D, MODE, KS, FMT_BF16, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
 }
 
 // out[i] = bf16(sum over s of part[s][i]), the parts of a split reduction added in order;
@@ -490,12 +812,15 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 // flight from the start (decode down 155.4 -> 153.9 us).  Where K is not a multiple of the
 // step they fall back to 256-value steps (KS_MID), then to 128-value steps, four in flight
 // (KS_ALT, D_ALT).
-template <int MF, int FMT, int MODE> struct FfnCfg {
-  static constexpr bool FP4 = FMT == FMT_MXFP4;
+// MXFP8 activations (ACT_MXFP8): 4 waves of two 16-row blocks each (gate/up rounds h in
+// blocks of 32 rows of one wave), 128-value steps.
+template <int MF, int FMT, int MODE, int ACT = ACT_BF16> struct FfnCfg {
+  static constexpr bool FP4 = FMT != FMT_BF16;  // MX weights (MXFP4 or MXFP8): 128-value steps
+  static constexpr bool A8 = ACT == ACT_MXFP8;
   static constexpr bool DOWN = MODE == MODE_DOWN;
   static constexpr bool WIDE = !FP4 && (MF == 1 || (MF == 2 && !DOWN));
-  static constexpr int NW = (MF <= 2 || DOWN) ? 4 : 8;
-  static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN) ? 2 : 1;
+  static constexpr int NW = (MF <= 2 || DOWN || A8) ? 4 : 8;
+  static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN || A8) ? 2 : 1;
   static constexpr int KS = FP4 ? 128 : WIDE ? ((MF == 1 && DOWN) ? 384 : 256) : 64;
   static constexpr int D = WIDE ? 2
                          : MF <= 2 ? (FP4 ? 3 : 4)
@@ -506,9 +831,10 @@ template <int MF, int FMT, int MODE> struct FfnCfg {
   static constexpr int KS_ALT = WIDE ? 128 : KS, D_ALT = WIDE ? 4 : D;
 };
 
-template <int MF, int MODE, int FMT>
+template <int MF, int MODE, int FMT, int ACT = ACT_BF16>
 hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Tracer* tr) {
-  using C = FfnCfg<MF, FMT, MODE>;
+  using C = FfnCfg<MF, FMT, MODE, ACT>;
+  if (ACT == ACT_MXFP8 && (a.ksplit != 1 || a.dense)) return hipErrorInvalidValue;
   constexpr int ROWS = C::NW * C::RF * 16;  // weight rows per block of each matrix
   if (a.bm_list % (16 * MF) || a.N % ROWS || a.ksplit < 1 || a.K % a.ksplit) return hipErrorInvalidValue;
   const int kspan = a.K / a.ksplit;
@@ -519,13 +845,14 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   int64_t grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   if (kspan % C::KS == 0)
-    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS>, dim3((unsigned)grid), dim3(C::NW * 64), s, a);
-  else if (C::KS_MID != C::KS && kspan % C::KS_MID == 0)
-    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS_MID>, dim3((unsigned)grid), dim3(C::NW * 64), s,
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS, ACT>, dim3((unsigned)grid), dim3(C::NW * 64), s,
            a);
-  else if (C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
-    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT>, dim3((unsigned)grid), dim3(C::NW * 64), s,
-           a);
+  else if (ACT == ACT_BF16 && C::KS_MID != C::KS && kspan % C::KS_MID == 0)
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS_MID, ACT>, dim3((unsigned)grid),
+           dim3(C::NW * 64), s, a);
+  else if (ACT == ACT_BF16 && C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
+    launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT, ACT>, dim3((unsigned)grid),
+           dim3(C::NW * 64), s, a);
   else
     return hipErrorInvalidValue;
   hipError_t err = hipGetLastError();
@@ -534,14 +861,38 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
 }
 
 template <int MODE>
-hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr) {
+hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr,
+                       int act = ACT_BF16) {
+  if (act == ACT_MXFP8) {
+#define MOE_A8(F)                                                                    \
+  switch (mf) {                                                                      \
+    case 1: return launch_one<1, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
+    case 2: return launch_one<2, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
+    case 4: return launch_one<4, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
+    case 8: return launch_one<8, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
+    default: return hipErrorInvalidValue;                                            \
+  }
+    if (fmt == FMT_MXFP4) MOE_A8(FMT_MXFP4)
+    if (fmt == FMT_MXFP8) MOE_A8(FMT_MXFP8)
+#undef MOE_A8
+    return hipErrorInvalidValue;  // MXFP8 activations need block-format weights
+  }
   if (fmt == FMT_MXFP4) {
     switch (mf) {
       case 1: return launch_one<1, MODE, FMT_MXFP4>(a, rbw, max_tiles, s, tr);
       case 2: return launch_one<2, MODE, FMT_MXFP4>(a, rbw, max_tiles, s, tr);
       case 4: return launch_one<4, MODE, FMT_MXFP4>(a, rbw, max_tiles, s, tr);
       case 8: return launch_one<8, MODE, FMT_MXFP4>(a, rbw, max_tiles, s, tr);
-      default: return hipErrorInvalidValue;  // the plan never picks 16 for MXFP4
+      default: return hipErrorInvalidValue;  // the plan never picks 16 for MX weights
+    }
+  }
+  if (fmt == FMT_MXFP8) {
+    switch (mf) {
+      case 1: return launch_one<1, MODE, FMT_MXFP8>(a, rbw, max_tiles, s, tr);
+      case 2: return launch_one<2, MODE, FMT_MXFP8>(a, rbw, max_tiles, s, tr);
+      case 4: return launch_one<4, MODE, FMT_MXFP8>(a, rbw, max_tiles, s, tr);
+      case 8: return launch_one<8, MODE, FMT_MXFP8>(a, rbw, max_tiles, s, tr);
+      default: return hipErrorInvalidValue;
     }
   }
   switch (mf) {
@@ -563,8 +914,9 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   // two waves per SIMD; gate/up with 128, or 256 when experts average well above 128 tokens;
   // MXFP4 experts with up to 96 tokens on average take 64-token tiles: at 64 per expert,
   // gate/up 0.694 -> 0.731 ms but down 0.606 -> 0.548 ms)
-  p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : (avg <= 48 || (fmt == FMT_MXFP4 && avg <= 96)) ? 4
-       : (avg <= 192 || fmt == FMT_MXFP4) ? 8 : 16;
+  const bool mx = fmt != FMT_BF16;  // MXFP8 weights take the MXFP4 tile sizes
+  p.mf = avg <= 12 ? 1 : avg <= 24 ? 2 : (avg <= 48 || (mx && avg <= 96)) ? 4
+       : (avg <= 192 || mx) ? 8 : 16;
   p.mf_gate_up = p.mf;
   p.mf_down = std::min(p.mf, 4);
   // more than 12 tokens per expert and bf16 weights: the 256-token tile kernel (ffn_tile.hip)
@@ -617,8 +969,10 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                              int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
                              float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
-                             bool tiles_ready, hipStream_t s, Tracer* tr) {
+                             bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab) {
   hipError_t err = hipSuccess;
+  const bool a8 = ab && ab->act == ACT_MXFP8;
+  if (a8 && (p.tiles || w.fmt == FMT_BF16 || !ab->xq || !ab->xs || !ab->hq || !ab->hs)) return hipErrorInvalidValue;
   if (p.tiles) {
     if (!tiles_ready) {
       launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix, tile_info_offset(E));
@@ -635,6 +989,14 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
     if (tr) tr->mark("expert_tiles", s);
   }
   if (err != hipSuccess) return err;
+  if (a8) {
+    // x rounded to MXFP8 once for all routed experts (the shared expert reads x as bf16)
+    const int64_t nblocks = (int64_t)T * H / 32;
+    launch(tr, mx8_quant_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), s, x, nblocks, ab->xq, ab->xs);
+    err = hipGetLastError();
+    if (tr) tr->mark("act_quant", s);
+    if (err != hipSuccess) return err;
+  }
 
   FfnArgs gu{};
   gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
@@ -652,9 +1014,23 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
 
   gu.bm_list = dn.bm_list = p.bm;
   gu.group_major = dn.group_major = p.group_major ? 1 : 0;
-  err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr);
+  const int act = a8 ? ACT_MXFP8 : ACT_BF16;
+  if (a8) {
+    gu.aq = ab->xq; gu.as = ab->xs; gu.oq = ab->hq; gu.os = ab->hs;
+    dn.aq = ab->hq; dn.as = ab->hs;
+  }
+  err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr, act);
   if (err != hipSuccess) return err;
-  return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr);
+  return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr, act);
+}
+
+hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (cols % 32 || rows < 0) return hipErrorInvalidValue;
+  const int64_t nblocks = rows * cols / 32;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx8_quant_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, x, nblocks, codes,
+                     scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,

@@ -78,8 +78,13 @@ moe_status_t validate_config(const moe_config_t* c, int64_t T) {
   if (c->num_shared_experts && c->shared_intermediate_size != c->moe_intermediate_size)
     return fail(MOE_ERR_UNSUPPORTED, "shared_intermediate_size %d must equal moe_intermediate_size %d",
                 c->shared_intermediate_size, c->moe_intermediate_size);
-  if (c->expert_weight_format != MOE_WEIGHTS_BF16 && c->expert_weight_format != MOE_WEIGHTS_MXFP4)
+  if (c->expert_weight_format != MOE_WEIGHTS_BF16 && c->expert_weight_format != MOE_WEIGHTS_MXFP4 &&
+      c->expert_weight_format != MOE_WEIGHTS_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "expert_weight_format %d is unknown", c->expert_weight_format);
+  if (c->expert_act_format != MOE_ACT_BF16 && c->expert_act_format != MOE_ACT_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "expert_act_format %d is unknown", c->expert_act_format);
+  if (c->expert_act_format == MOE_ACT_MXFP8 && c->expert_weight_format == MOE_WEIGHTS_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP8 activations need MXFP4 or MXFP8 expert weights");
   if (!std::isfinite(c->routed_scaling_factor)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor is not finite");
   if (std::isnan(c->swiglu_limit) || std::isnan(c->shared_swiglu_limit))
     return fail(MOE_ERR_INVALID_ARG, "swiglu limits must not be NaN");
@@ -90,9 +95,16 @@ moe_status_t validate_config(const moe_config_t* c, int64_t T) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// the kernels' weight-format code (moe_weight_format_t values are the same numbers)
+int wfmt(const moe_config_t* c) {
+  return c->expert_weight_format == MOE_WEIGHTS_MXFP4   ? moe::FMT_MXFP4
+         : c->expert_weight_format == MOE_WEIGHTS_MXFP8 ? moe::FMT_MXFP8
+                                                         : moe::FMT_BF16;
+}
+
 struct Layout {
   size_t partial, bitmap, counts, counts_out, offsets, tile_prefix, topk_idx, topk_w, sorted_token, inv_perm, h_hi, h_lo, y,
-      total;
+      xq, xs, hq, hs, total;
 };
 
 Layout layout(const moe_config_t* c, int64_t T) {
@@ -114,8 +126,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
   // the FFN tile prefix and, after it, one 16-byte record per tile of the plan
   L.tile_prefix = take(((size_t)moe::tile_info_offset((int)E) +
                         4 * (size_t)moe::ffn_plan(T, (int)K, (int)E, (int)S,
-                                                  c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4
-                                                                                               : moe::FMT_BF16,
+                                                  wfmt(c),
                                                   (int)H, (int)I).max_tiles) * 4);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
@@ -124,6 +135,12 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.h_hi = take(P * I * 2);
   L.h_lo = take(P * I * 2);
   L.y = take(P * H * 4);
+  // MXFP8 activations: x and h as E4M3 codes and e8m0 scales (empty otherwise)
+  const bool a8 = c->expert_act_format == MOE_ACT_MXFP8;
+  L.xq = take(a8 ? T * H : 0);
+  L.xs = take(a8 ? T * H / 32 : 0);
+  L.hq = take(a8 ? P * I : 0);
+  L.hs = take(a8 ? P * I / 32 : 0);
   L.total = off;
   return L;
 }
@@ -143,9 +160,9 @@ moe_status_t check_weights(const moe_config_t* c, const moe_expert_weights_t* w)
   MOE_CHECK_PTR(w->gate, "weights->gate");
   MOE_CHECK_PTR(w->up, "weights->up");
   MOE_CHECK_PTR(w->down, "weights->down");
-  if (c->expert_weight_format == MOE_WEIGHTS_MXFP4) {
+  if (c->expert_weight_format != MOE_WEIGHTS_BF16) {
     if (!w->gate_scale || !w->up_scale || !w->down_scale)
-      return fail(MOE_ERR_INVALID_ARG, "MXFP4 weights need gate_scale, up_scale and down_scale");
+      return fail(MOE_ERR_INVALID_ARG, "MXFP4 and MXFP8 weights need gate_scale, up_scale and down_scale");
   }
   if (c->num_shared_experts) {
     MOE_CHECK_PTR(w->shared_gate, "weights->shared_gate");
@@ -160,7 +177,7 @@ moe::FfnWeights ffn_weights(const moe_config_t* c, const moe_expert_weights_t* w
   f.gate = w->gate; f.up = w->up; f.down = w->down;
   f.gate_scale = w->gate_scale; f.up_scale = w->up_scale; f.down_scale = w->down_scale;
   f.sh_gate = w->shared_gate; f.sh_up = w->shared_up; f.sh_down = w->shared_down;
-  f.fmt = c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16;
+  f.fmt = wfmt(c);
   return f;
 }
 
@@ -199,7 +216,7 @@ moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, i
                          int32_t* sorted_token, int32_t* inv_perm, const Layout& L, void* ws, hipStream_t s,
                          moe::Tracer* tr = nullptr, bool marked = false, bool with_tiles = false) {
   moe::FfnPlan fp = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
-                                   c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                                   wfmt(c),
                                    c->hidden_size, c->moe_intermediate_size);
   int32_t* hist = marked ? (int32_t*)at(ws, L.counts) : counts;
   hipError_t e = moe::launch_dispatch(idx, (int)T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
@@ -213,14 +230,22 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32
                     const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
                     hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false) {
   moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
-                                  c->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                                  wfmt(c),
                                   c->hidden_size, c->moe_intermediate_size);
   const float lim = c->swiglu_limit > 0 ? c->swiglu_limit : 0.f;
   const float slim = c->shared_swiglu_limit > 0 ? c->shared_swiglu_limit : 0.f;
+  moe::ActBufs ab;
+  if (c->expert_act_format == MOE_ACT_MXFP8) {
+    ab.act = moe::ACT_MXFP8;
+    ab.xq = (uint8_t*)at(ws, L.xq);
+    ab.xs = (uint8_t*)at(ws, L.xs);
+    ab.hq = (uint8_t*)at(ws, L.hq);
+    ab.hs = (uint8_t*)at(ws, L.hs);
+  }
   hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),
                                         ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
                                         c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
-                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr);
+                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr, &ab);
   if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   return MOE_OK;
 }
@@ -419,6 +444,20 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
   return do_combine(&dc, T, y, inv, wts, out, s);
 }
 
+moe_status_t moe_quantise_mxfp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                                void* stream) {
+  g_last_error.clear();
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows = %lld must be >= 0", (long long)rows);
+  if (cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "cols = %d must be a positive multiple of 32", cols);
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(codes, "codes");
+  if (!scales) return fail(MOE_ERR_INVALID_ARG, "scales must not be NULL");
+  hipError_t e = moe::launch_mx8_quant((const uint16_t*)x, rows, cols, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "MXFP8 quantise launch");
+  return MOE_OK;
+}
+
 moe_status_t moe_update_expert_bias(const moe_config_t* cfg, const int32_t* expert_counts, float* expert_bias,
                                     float gamma, void* stream) {
   g_last_error.clear();
@@ -486,7 +525,7 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
     fd.tile_prefix = (int32_t*)at(ws, L.tile_prefix);
     fd.S = cfg->num_shared_experts;
     fd.bm = moe::ffn_plan(T, cfg->num_experts_per_tok, cfg->num_experts, cfg->num_shared_experts,
-                          cfg->expert_weight_format == MOE_WEIGHTS_MXFP4 ? moe::FMT_MXFP4 : moe::FMT_BF16,
+                          wfmt(cfg),
                           cfg->hidden_size, cfg->moe_intermediate_size).bm;
     if ((st = do_route(cfg, T, x, router_w, expert_bias, idx, wts, L, ws, s, tr, true, &fd)) != MOE_OK) return st;
   } else {

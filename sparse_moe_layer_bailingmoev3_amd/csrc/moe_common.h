@@ -44,6 +44,30 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// ---- MXFP8 (OCP MX v1.0, E4M3 elements, one e8m0 scale per 32 values) ----------------
+// Shared-scale byte of a block from its largest magnitude: X = floor(log2 amax) - 8 (8 = the
+// exponent of E4M3's largest normal, 448), clamped to [-127, 127], stored as X + 127; an
+// all-zero block (or one below fp32's normal range) gets X = -127.
+__device__ __forceinline__ int mx8_scale_byte(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);  // biased exponent: floor(log2) + 127
+  if (ef == 0) return 0;
+  return min(254, max(0, ef - 8));
+}
+
+// Four values of a block with shared exponent X (= scale byte - 127) -> four E4M3 codes, low
+// byte first: v * 2^-X (exact), clamped to +-448 so nothing overflows, then gfx950's fp32 ->
+// E4M3 conversion (round to nearest even).
+__device__ __forceinline__ uint32_t mx8_pack4(float v0, float v1, float v2, float v3, int X) {
+  const float c = 448.0f;
+  v0 = fminf(fmaxf(__builtin_amdgcn_ldexpf(v0, -X), -c), c);
+  v1 = fminf(fmaxf(__builtin_amdgcn_ldexpf(v1, -X), -c), c);
+  v2 = fminf(fmaxf(__builtin_amdgcn_ldexpf(v2, -X), -c), c);
+  v3 = fminf(fmaxf(__builtin_amdgcn_ldexpf(v3, -X), -c), c);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+  return (uint32_t)w;
+}
+
 // Map a linear block id to a work id so that consecutive work ids run on the same
 // XCD: the hardware deals blocks round-robin over the 8 XCDs, so block b lands on
 // XCD b % 8.  `nblocks` must be a multiple of 8.

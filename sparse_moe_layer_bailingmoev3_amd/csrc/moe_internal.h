@@ -7,7 +7,10 @@
 
 namespace moe {
 
-enum { FMT_BF16 = 0, FMT_MXFP4 = 1 };
+// routed-expert weight formats (moe_weight_format_t values)
+enum { FMT_BF16 = 0, FMT_MXFP4 = 1, FMT_MXFP8 = 2 };
+// activations of the routed experts' products (moe_act_format_t values)
+enum { ACT_BF16 = 0, ACT_MXFP8 = 1 };
 
 // The FFN tile list: tile_prefix[0 .. E+1] (tiles of the experts before e), then, from this
 // offset (in int32, 16-byte aligned), one record per tile: {expert, its first sorted
@@ -120,11 +123,24 @@ struct FfnPlan {
   int64_t max_tiles;
 };
 FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I);
+// MXFP8 activations of the routed experts (act == ACT_MXFP8): x rounded to MXFP8 (codes [T,H],
+// scales [T,H/32]) by a first kernel, h written by gate/up as MXFP8 (codes [P,I], scales
+// [P,I/32]); the shared expert keeps bf16 x and the two bf16 h planes
+struct ActBufs {
+  int act = ACT_BF16;
+  uint8_t* xq = nullptr;
+  uint8_t* xs = nullptr;
+  uint8_t* hq = nullptr;
+  uint8_t* hs = nullptr;
+};
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
                              const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
-                             Tracer* tr = nullptr);
+                             Tracer* tr = nullptr, const ActBufs* ab = nullptr);
+// bf16 [rows, cols] -> MXFP8 codes [rows, cols] and e8m0 scales [rows, cols/32] (cols % 32 == 0)
+hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s);
 
 // a dense FFN (one weight set, every token, weight 1) on the expert FFN kernels without the
 // dispatch and combine: tiles follow from T, down writes the bf16 output [T,H] (plan from

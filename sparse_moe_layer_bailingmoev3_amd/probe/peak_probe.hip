@@ -14,17 +14,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t NEVER = 0x9E3779B9u;  // a sink value the data never produces in practice
 
-// sum of n 16-byte elements, four loads in flight per lane; one word per workgroup is written
-// only if the xor of its data equals NEVER, which keeps every load live
+// xor of n 16-byte elements: each workgroup reads spans of 8 x 4 KB (a wave instruction covers
+// 1 KB), the 8 loads of a span in flight together; one word per workgroup is written only if
+// the xor of its data equals NEVER, which keeps every load live
+constexpr int RU = 8;
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, size_t n, uint32_t* __restrict__ sink) {
   u32x4 acc = {0u, 0u, 0u, 0u};
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+  const size_t span = (size_t)RU * 256, stride = (size_t)gridDim.x * span;
+  for (size_t base = (size_t)blockIdx.x * span; base < n; base += stride) {
+    u32x4 v[RU];
+#pragma unroll
+    for (int j = 0; j < RU; ++j) {
+      const size_t i = base + j * 256 + threadIdx.x;
+      v[j] = i < n ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < RU; ++j) acc ^= v[j];
   }
-  for (; i < n; i += stride) acc ^= src[i];
   const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (r == NEVER) sink[blockIdx.x] = r;
 }

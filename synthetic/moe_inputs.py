@@ -53,7 +53,8 @@ class LayerShape:
     num_shared_experts: int = 1
     swiglu_limit: float = 0.0          # <= 0: no clamp
     shared_swiglu_limit: float = 0.0   # <= 0: no clamp
-    weight_format: str = "bf16"        # "bf16" | "mxfp4" (routed experts only)
+    weight_format: str = "bf16"        # "bf16" | "mxfp4" | "mxfp8" (routed experts only)
+    act_format: str = "bf16"           # "bf16" | "mxfp8": activations of the routed experts' products
     x_dist: str = "normal"             # "normal" | "clusters"
     bias_dist: str = "uniform"         # "uniform" U(-0.1,0.1) | "normal" N(0,0.5) | "zero"
     weight_std: float = 0.02
@@ -91,6 +92,11 @@ CONFIGS = {
     "skewed": LayerShape("skewed", T=16384, **_FULL, swiglu_limit=4.0, shared_swiglu_limit=7.0,
                          x_dist="clusters", bias_dist="normal"),
     "mxfp4": LayerShape("mxfp4", T=4096, **_FULL, weight_format="mxfp4"),
+    # the "FP8 + MXFP4" variants: routed experts in MXFP8 (bf16 activations), and MXFP4 or
+    # MXFP8 routed experts with MXFP8 activations (scaled MFMA)
+    "mxfp8": LayerShape("mxfp8", T=4096, **_FULL, weight_format="mxfp8"),
+    "mxfp4_a8": LayerShape("mxfp4_a8", T=4096, **_FULL, weight_format="mxfp4", act_format="mxfp8"),
+    "mxfp8_a8": LayerShape("mxfp8_a8", T=4096, **_FULL, weight_format="mxfp8", act_format="mxfp8"),
 }
 
 
@@ -196,14 +202,17 @@ def gen_shared(shape: LayerShape, seed: int = 0) -> dict:
 def gen_experts(shape: LayerShape, seed: int = 0, threads: int | None = None) -> dict:
     """All routed experts stacked: gate [E,I,H], up [E,I,H], down [E,H,I] (bf16 bits).
 
-    For weight_format == "mxfp4" the stacked arrays are the MXFP4 encoding instead:
-    gate_q [E,I,H/2], gate_s [E,I,H/32], ... (see quantise_mxfp4)."""
+    For weight_format "mxfp4" / "mxfp8" the stacked arrays are that encoding instead:
+    gate_q [E,I,H/2] (MXFP4) or [E,I,H] (MXFP8), gate_s [E,I,H/32], ... (see quantise_mxfp4,
+    quantise_mxfp8)."""
     E, I, H = shape.E, shape.I, shape.H
-    mx = shape.weight_format == "mxfp4"
+    mx = shape.weight_format in ("mxfp4", "mxfp8")
+    quant = quantise_mxfp4 if shape.weight_format == "mxfp4" else quantise_mxfp8
     if mx:
-        out = dict(gate_q=np.empty((E, I, H // 2), np.uint8), gate_s=np.empty((E, I, H // 32), np.uint8),
-                   up_q=np.empty((E, I, H // 2), np.uint8), up_s=np.empty((E, I, H // 32), np.uint8),
-                   down_q=np.empty((E, H, I // 2), np.uint8), down_s=np.empty((E, H, I // 32), np.uint8))
+        cd = 2 if shape.weight_format == "mxfp4" else 1  # values per byte
+        out = dict(gate_q=np.empty((E, I, H // cd), np.uint8), gate_s=np.empty((E, I, H // 32), np.uint8),
+                   up_q=np.empty((E, I, H // cd), np.uint8), up_s=np.empty((E, I, H // 32), np.uint8),
+                   down_q=np.empty((E, H, I // cd), np.uint8), down_s=np.empty((E, H, I // 32), np.uint8))
     else:
         out = dict(gate=np.empty((E, I, H), np.uint16), up=np.empty((E, I, H), np.uint16),
                    down=np.empty((E, H, I), np.uint16))
@@ -212,7 +221,7 @@ def gen_experts(shape: LayerShape, seed: int = 0, threads: int | None = None) ->
         w = gen_expert(shape, e, seed)
         if mx:
             for k in ("gate", "up", "down"):
-                q, s = quantise_mxfp4(w[k])
+                q, s = quant(w[k])
                 out[k + "_q"][e], out[k + "_s"][e] = q, s
         else:
             for k in ("gate", "up", "down"):
@@ -226,11 +235,12 @@ def gen_experts(shape: LayerShape, seed: int = 0, threads: int | None = None) ->
 def gen_expert_encoded(shape: LayerShape, e: int, seed: int = 0) -> dict:
     """One routed expert in the workload's storage format (bf16 bits or MXFP4 pieces)."""
     w = gen_expert(shape, e, seed)
-    if shape.weight_format != "mxfp4":
+    if shape.weight_format == "bf16":
         return w
+    quant = quantise_mxfp4 if shape.weight_format == "mxfp4" else quantise_mxfp8
     out = {}
     for k in ("gate", "up", "down"):
-        out[k + "_q"], out[k + "_s"] = quantise_mxfp4(w[k])
+        out[k + "_q"], out[k + "_s"] = quant(w[k])
     return out
 
 
@@ -270,6 +280,40 @@ def quantise_mxfp4(w_bits: np.ndarray):
     packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     scales = (X + 127).astype(np.uint8)
     return packed, scales
+
+
+def quantise_mxfp8(w_bits: np.ndarray):
+    """bf16 weight [N, K] -> (E4M3 codes uint8 [N, K], e8m0 scales uint8 [N, K/32]).
+
+    The OCP Microscaling (MX) v1.0 conversion with E4M3 elements: per block of 32 consecutive
+    K values, X = floor(log2(max|v|)) - 8 (8 = the exponent of E4M3's largest normal, 448);
+    each v / 2^X is rounded to nearest on the E4M3 grid of its binade (3 mantissa bits; below
+    2^-6 the fixed subnormal step 2^-9), ties to even, and saturated at 448.  Code = sign<<7 |
+    exponent (bias 7) << 3 | mantissa.  An all-zero block gets X = -127."""
+    v = bf16_bits_to_f32(w_bits).astype(np.float64)
+    N, K = v.shape
+    assert K % 32 == 0
+    blk = v.reshape(N, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127).astype(np.int64)
+    X = np.clip(X, -127, 127)
+    mag = np.abs(blk) / np.exp2(X.astype(np.float64))[:, :, None]
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    ex = np.clip(ex, -6, 8)                      # binade (subnormals share the step of 2^-6)
+    step = np.exp2(ex - 3)
+    q = np.minimum(np.rint(mag / step) * step, 448.0)   # rint: ties to even
+    # encode q: a rounding up may have reached the next binade, so take its exponent again
+    with np.errstate(divide="ignore"):
+        eq = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    sub = q < 2.0 ** -6
+    e_field = np.where(sub, 0, eq + 7)
+    m_field = np.where(sub, q / 2.0 ** -9, (q / np.exp2(eq) - 1.0) * 8)
+    code = (e_field.astype(np.int64) << 3) | m_field.astype(np.int64)
+    sign = (blk < 0) & (code != 0)
+    codes = (code | (sign.astype(np.int64) << 7)).astype(np.uint8).reshape(N, K)
+    return codes, (X + 127).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------------

@@ -14,14 +14,19 @@ from synthetic import (LayerShape, gen_bias, gen_expert_encoded, gen_experts, ge
 TIE_EPS = 1e-6
 
 
+WEIGHT_FORMATS = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}   # moe_weight_format_t
+ACT_FORMATS = {"bf16": 0, "mxfp8": 1}                   # moe_act_format_t
+
+
 def cfg_for(shape: LayerShape):
-    from sparse_moe_layer_bailingmoev3_amd import MOE_WEIGHTS_BF16, MOE_WEIGHTS_MXFP4, MoEConfig
+    from sparse_moe_layer_bailingmoev3_amd import MoEConfig
     return MoEConfig(hidden_size=shape.H, num_experts=shape.E, num_experts_per_tok=shape.K, n_group=shape.G,
                      topk_group=shape.TG, moe_intermediate_size=shape.I,
                      num_shared_experts=shape.num_shared_experts, shared_intermediate_size=shape.I_s,
                      norm_topk_prob=int(shape.norm_topk_prob), routed_scaling_factor=shape.routed_scaling_factor,
                      swiglu_limit=shape.swiglu_limit, shared_swiglu_limit=shape.shared_swiglu_limit,
-                     expert_weight_format=MOE_WEIGHTS_MXFP4 if shape.weight_format == "mxfp4" else MOE_WEIGHTS_BF16)
+                     expert_weight_format=WEIGHT_FORMATS[shape.weight_format],
+                     expert_act_format=ACT_FORMATS[shape.act_format])
 
 
 @dataclasses.dataclass
@@ -52,9 +57,10 @@ class HostCase:
         self._cache = dict(zip(todo, dec))
 
     def _decode(self, e: int):
-        if self.shape.weight_format == "mxfp4":
+        if self.shape.weight_format in ("mxfp4", "mxfp8"):
             ex = self.experts
-            return tuple(oracle.mxfp4_dequant(ex[k + "_q"][e], ex[k + "_s"][e]) for k in ("gate", "up", "down"))
+            dq = oracle.mxfp4_dequant if self.shape.weight_format == "mxfp4" else oracle.mxfp8_dequant
+            return tuple(dq(ex[k + "_q"][e], ex[k + "_s"][e]) for k in ("gate", "up", "down"))
         return tuple(oracle.bf16_to_f64(self.experts[k][e]) for k in ("gate", "up", "down"))
 
     def shared_f64(self):
@@ -90,7 +96,8 @@ def oracle_forward(c: HostCase, rows=None):
     return oracle.moe_layer(x, c.router_w, c.bias, c.expert_f64, c.shared_f64(), n_group=s.G,
                             topk_group=s.TG, top_k=s.K, routed_scaling_factor=s.routed_scaling_factor,
                             norm_topk_prob=s.norm_topk_prob, swiglu_limit=s.swiglu_limit,
-                            shared_swiglu_limit=s.shared_swiglu_limit)
+                            shared_swiglu_limit=s.shared_swiglu_limit,
+                            act_quant="mxfp8" if s.act_format == "mxfp8" else "none")
 
 
 # ----------------------------------------------------------------------------------
@@ -120,7 +127,7 @@ class DeviceCase:
         self.router_w = to_dev(c.router_w)
         self.bias = to_dev(c.bias)
         sh = [to_dev(c.shared[k], bf16=True) for k in ("gate", "up", "down")] if s.num_shared_experts else [None] * 3
-        if s.weight_format == "mxfp4":
+        if s.weight_format in ("mxfp4", "mxfp8"):
             ex = c.experts
             self.weights = MoEExpertWeights(to_dev(ex["gate_q"]), to_dev(ex["up_q"]), to_dev(ex["down_q"]),
                                             to_dev(ex["gate_s"]), to_dev(ex["up_s"]), to_dev(ex["down_s"]), *sh)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import CONFIGS, gen_experts, quantise_mxfp4
+from synthetic import CONFIGS, gen_experts, quantise_mxfp4, quantise_mxfp8
 
 from moe_case import (DeviceCase, compare_routing, expected_counts, host_case, oracle_forward, oracle_route, rms,
                       to_bits, to_dev)
@@ -219,6 +219,72 @@ def test_forward_tiny_mxfp4(T, limit):
         ex[k + "_q"] = np.stack([a for a, _ in qs])
         ex[k + "_s"] = np.stack([b for _, b in qs])
     check_forward(host_case(s, seed=16, T=T, experts=ex), tol=TOL_MXFP4)
+
+
+def _tiny_block_experts(fmt, seed):
+    """The tiny layer's bf16 experts encoded in a block format (MXFP4 or MXFP8)."""
+    quant = quantise_mxfp4 if fmt == "mxfp4" else quantise_mxfp8
+    bf = gen_experts(CONFIGS["tiny"], seed=seed)
+    ex = {}
+    for k in ("gate", "up", "down"):
+        qs = [quant(bf[k][e]) for e in range(CONFIGS["tiny"].E)]
+        ex[k + "_q"] = np.stack([a for a, _ in qs])
+        ex[k + "_s"] = np.stack([b for _, b in qs])
+    return ex
+
+
+# MXFP8 weights decoded exactly to bf16: the bf16 bar.  T = 40: 16-token tiles, 600: 64-token
+# tiles, 1000: 128-token tiles; clamped on both epilogues
+@pytest.mark.parametrize("T,limit", [(40, 0.0), (600, 0.0), (1000, 0.0), (40, 0.002), (600, 0.002)])
+def test_forward_tiny_mxfp8(T, limit):
+    s = CONFIGS["tiny"].with_(weight_format="mxfp8")
+    if limit:
+        s = s.with_(swiglu_limit=limit, shared_swiglu_limit=1.5 * limit)
+    check_forward(host_case(s, seed=22, T=T, experts=_tiny_block_experts("mxfp8", 22)), tol=TOL_BF16)
+
+
+def test_quantise_mxfp8_bit_exact():
+    """The device MXFP8 rounding (moe_quantise_mxfp8, the code the 8-bit-activation path runs on
+    x and, in the gate/up epilogue, on h) against the oracle's quantiser, code for code and
+    scale for scale: bf16 rows over 2^-133 .. 2^20, exact ties between E4M3 neighbours,
+    saturating blocks, all-zero blocks and bf16 subnormals."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    from synthetic import f32_to_bf16_bits
+    rng = np.random.default_rng(23)
+    R, C = 96, 512
+    v = rng.standard_normal((R, C)) * np.exp2(rng.integers(-40, 20, size=(R, 1)))
+    v[1] = 0.0
+    v[2, :32] = 2.0 ** -133 * np.arange(32)                      # bf16 subnormals
+    ties = np.array([1.0625, 1.1875, 1.3125, -1.4375, 3.25, 0.2578125, 448 / 256, 480 / 256])
+    v[3, :32] = 1.0
+    v[3, 1:1 + ties.size] = ties                                  # amax 1 -> scaled by 256: ties and 448, 480
+    v[4, :32] = np.linspace(-1.9, 1.9, 32)                        # saturation at both ends
+    bits = f32_to_bf16_bits(v.astype(np.float32))
+    say(f"[gpu] moe_quantise_mxfp8 {R}x{C}")
+    x = to_dev(bits, bf16=True)
+    codes = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
+    moe.moe_quantise_mxfp8(x, R, C, codes, scales)
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mxfp8_quantise(oracle.bf16_to_f64(bits))
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
+    got = codes.cpu().numpy()
+    # +0 and -0 are the same value: compare decoded values, and codes where the value is nonzero
+    np.testing.assert_array_equal(oracle.e4m3_value(got), oracle.e4m3_value(want_c))
+    nz = oracle.e4m3_value(want_c) != 0
+    np.testing.assert_array_equal(got[nz], want_c[nz])
+
+
+# MXFP8 activations on the routed experts (scaled MFMA), against the oracle's act_quant="mxfp8"
+# mode; MXFP4 and MXFP8 weights; 16-, 64- and 128-token tiles; the clamp before h's rounding
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("T,limit", [(40, 0.0), (600, 0.0), (1000, 0.0), (40, 0.002), (3000, 0.002)])
+def test_forward_tiny_act_mxfp8(wfmt, T, limit):
+    s = CONFIGS["tiny"].with_(weight_format=wfmt, act_format="mxfp8")
+    if limit:
+        s = s.with_(swiglu_limit=limit, shared_swiglu_limit=1.5 * limit)
+    check_forward(host_case(s, seed=24, T=T, experts=_tiny_block_experts(wfmt, 24)), tol=TOL_MXFP4)
 
 
 def test_determinism_tiny_tiles():
@@ -540,3 +606,47 @@ def test_forward_mxfp4_full(full_experts):
         list(pool.map(q, range(E)))
     c = host_case(s, seed=0, experts=ex)
     check_forward(c, rows=tile_rows(64), tol=TOL_MXFP4)  # 64-token tiles at 64 tokens per expert
+
+
+@pytest.mark.slow
+def test_forward_mxfp8_full(full_experts):
+    from concurrent.futures import ThreadPoolExecutor
+    s = CONFIGS["mxfp8"]
+    E, I, H = s.E, s.I, s.H
+    ex = dict(gate_q=np.empty((E, I, H), np.uint8), gate_s=np.empty((E, I, H // 32), np.uint8),
+              up_q=np.empty((E, I, H), np.uint8), up_s=np.empty((E, I, H // 32), np.uint8),
+              down_q=np.empty((E, H, I), np.uint8), down_s=np.empty((E, H, I // 32), np.uint8))
+
+    def q(e):
+        for k in ("gate", "up", "down"):
+            ex[k + "_q"][e], ex[k + "_s"][e] = quantise_mxfp8(full_experts[k][e])
+    say("[host] quantising the 512 experts to MXFP8")
+    with ThreadPoolExecutor(16) as pool:
+        list(pool.map(q, range(E)))
+    c = host_case(s, seed=0, experts=ex)
+    check_forward(c, rows=tile_rows(64), tol=TOL_BF16)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
+def test_forward_act_mxfp8_full(full_experts, wfmt):
+    """The full-size layer with MXFP4 / MXFP8 routed experts and MXFP8 activations at T = 4096
+    (64-token tiles), against the oracle's 8-bit-activation mode on every tile's first and
+    last token."""
+    from concurrent.futures import ThreadPoolExecutor
+    s = CONFIGS[wfmt + "_a8"]
+    E, I, H = s.E, s.I, s.H
+    cd = 2 if wfmt == "mxfp4" else 1
+    quant = quantise_mxfp4 if wfmt == "mxfp4" else quantise_mxfp8
+    ex = dict(gate_q=np.empty((E, I, H // cd), np.uint8), gate_s=np.empty((E, I, H // 32), np.uint8),
+              up_q=np.empty((E, I, H // cd), np.uint8), up_s=np.empty((E, I, H // 32), np.uint8),
+              down_q=np.empty((E, H, I // cd), np.uint8), down_s=np.empty((E, H, I // 32), np.uint8))
+
+    def q(e):
+        for k in ("gate", "up", "down"):
+            ex[k + "_q"][e], ex[k + "_s"][e] = quant(full_experts[k][e])
+    say(f"[host] quantising the 512 experts to {wfmt}")
+    with ThreadPoolExecutor(16) as pool:
+        list(pool.map(q, range(E)))
+    c = host_case(s, seed=0, experts=ex)
+    check_forward(c, rows=tile_rows(64), tol=TOL_MXFP4)
