@@ -26,6 +26,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s (the scaled MFMA with an E4M3 operand)
+
+
+def mfma_peak(shape):
+    return FP8_PEAK_TFLOPS if shape.act_format == "mxfp8" else BF16_PEAK_TFLOPS
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -356,24 +361,34 @@ def roofline(shape, r, workload=None, measured=None):
     per_mat = eb // 3
     sh_mat = 2 * H * I  # shared expert is bf16
     dom = r["dom"]
+    routed = T * K
+    if shape.weight_format != "bf16":
+        # block-format weights: the timed launch is the routed experts' alone (the shared expert
+        # runs in bf16 launches of its own)
+        S, pairs = 0, routed
+    if shape.act_format == "mxfp8":
+        # x and h move as E4M3 codes plus one scale byte per 32 values
+        x_b, h_b = T * H * 33 // 32, routed * I * 33 // 32
+    else:
+        x_b, h_b = T * H * 2, pairs * I * 2
     if dom == "expert_gate_up":
-        byts = touched * 2 * per_mat + S * 2 * sh_mat + T * H * 2 + pairs * I * 2
+        byts = touched * 2 * per_mat + S * 2 * sh_mat + x_b + h_b
         flops = 4.0 * H * I * pairs
     else:
-        byts = touched * per_mat + S * sh_mat + pairs * I * 2 + pairs * H * 4
+        byts = touched * per_mat + S * sh_mat + h_b + pairs * H * 4
         flops = 2.0 * H * I * pairs
     ms = r["dom_ms"]
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     hbm_time = byts / (HBM_PEAK_GBS * 1e9)
-    mfma_time = flops / (BF16_PEAK_TFLOPS * 1e12)
+    mpeak = mfma_peak(shape)
+    mfma_time = flops / (mpeak * 1e12)
     if hbm_time >= mfma_time:
         rl = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
     else:
-        rl = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                  frac=round(tflops / BF16_PEAK_TFLOPS, 4))
+        rl = dict(bound="mfma", achieved=round(tflops, 1), peak=mpeak, unit="TFLOP/s", frac=round(tflops / mpeak, 4))
     rl.update(kernel=dom, kernel_ms=round(ms, 4), kernel_ms_dist=r.get("dom_dist"), algorithmic_bytes=int(byts),
-              bf16_flops=flops, touched_experts=touched, traffic=recorded_traffic(workload or shape.name, dom))
+              flops=flops, touched_experts=touched, traffic=recorded_traffic(workload or shape.name, dom))
     if measured:
         # HBM-bound kernels here mostly read: the measured read rate is their ceiling
         rl["frac_of_measured"] = round(gbs / measured["read_GBps"], 4) if rl["bound"] == "hbm" else \
@@ -440,9 +455,10 @@ def layer_summary(shape, r, measured=None):
     byts = touched * expert_bytes(shape) + S * 3 * H * I * 2 + E * H * 4 + E * 4 + 2 * T * H * 2
     flops = 6.0 * H * I * (T * K + T * S)
     ms = r["wall_ms"]
-    hbm_t, mfma_t = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+    hbm_t, mfma_t = byts / (HBM_PEAK_GBS * 1e9), flops / (mfma_peak(shape) * 1e12)
     return dict(algorithmic_bytes=int(byts), hbm_frac=round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                bf16_flops=flops, mfma_frac=round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                flops=flops, mfma_peak_TFLOPs=mfma_peak(shape),
+                mfma_frac=round(flops / (ms * 1e-3) / (mfma_peak(shape) * 1e12), 4),
                 binding_roofline_frac=round(max(hbm_t, mfma_t) / (ms * 1e-3), 4),
                 hbm_frac_of_measured_read=round(byts / (ms * 1e-3) / 1e9 / measured["read_GBps"], 4) if measured else None,
                 router_fp32_flops=2.0 * T * H * E, touched_experts=touched, step_ms_dist=r.get("step_dist"),
@@ -505,7 +521,7 @@ SYMBOL_STEPS = [(r"^ffn_tile_kernel<0,", "expert_gate_up"), (r"^ffn_tile_kernel<
                 (r"^router_logits_(kwaves_)?kernel", "router_logits"), (r"^router_topk_kernel", "router_topk"),
                 (r"^fill_u32_kernel", "dispatch_clear"), (r"^dispatch_mark_kernel", "dispatch_mark"),
                 (r"^dispatch_finish_kernel", "dispatch_finish"), (r"^dispatch_count_kernel", "dispatch_count"),
-                (r"^tile_prefix_kernel", "expert_tiles"),
+                (r"^tile_prefix_kernel", "expert_tiles"), (r"^mx8_quant_kernel", "act_quant"),
                 (r"^combine_kernel", "combine"), (r"^__amd_rocclr_copyBuffer", "copy")]
 
 
@@ -564,8 +580,15 @@ def summarize(src: str, workload: str):
     copy_f, copy_w = max(fetch["__amd_rocclr_copyBuffer"]), max(write["__amd_rocclr_copyBuffer"])
     sf, sw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
     steps = {}
-    for sym, c, avg, pct in stats:
+    # a step launched twice (the routed and the shared experts' kernels on the MXFP8-activation
+    # path) keeps its longer launch under its name and the other as <step>_shared
+    seen = {}
+    for sym, c, avg, pct in sorted(stats, key=lambda t: -t[2]):
         st = _step(sym)
+        if st in ("expert_gate_up", "expert_down"):
+            seen[st] = seen.get(st, 0) + 1
+            if seen[st] > 1:
+                st += "_shared"
         if st and st != "copy":
             steps[st] = dict(symbol=sym, calls=c, avg_us=avg, pct=pct,
                              fetch_bytes=float(np.mean(fetch.get(sym, [0.0]))) * 1024 * sf,
@@ -579,7 +602,8 @@ def summarize(src: str, workload: str):
              *cmds, "```", "", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
              "| kernel | step | calls | average us | % of GPU time |", "|---|---|---|---|---|"]
     for sym, c, avg, pct in stats:
-        lines.append(f"| `{sym}` | {_step(sym) or ''} | {c} | {avg:.1f} | {pct:.1f} |")
+        st = next((k for k, e in steps.items() if e["symbol"] == sym), _step(sym) or "")
+        lines.append(f"| `{sym}` | {st} | {c} | {avg:.1f} | {pct:.1f} |")
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
               f"A plain 1 GiB device copy in the same runs reads FETCH_SIZE = {copy_f:.0f} KiB and "
               f"WRITE_SIZE = {copy_w:.0f} KiB, so bytes = FETCH_SIZE * 1024 * {sf:.3f} and "
@@ -728,34 +752,42 @@ def main():
         from synthetic import quantise_mxfp4
         from concurrent.futures import ThreadPoolExecutor
         line["secondary"] = {}
-        for name in ("prefill", "skewed", "mxfp4"):
-            p = CONFIGS[name]
-            ex = experts
-            if p.weight_format == "mxfp4":
-                log("quantising the experts to MXFP4 ...")
-                ex = {k + sfx: np.empty((p.E,) + experts[k].shape[1:2] + (experts[k].shape[2] // div,), np.uint8)
-                      for k in ("gate", "up", "down") for sfx, div in (("_q", 2), ("_s", 32))}
+        from synthetic import quantise_mxfp8
+        quantised = {}
+
+        def encoded(fmt):
+            # the bf16 draw in a block format, once per format (as gen_experts would encode it)
+            if fmt not in quantised:
+                log(f"quantising the experts to {fmt} ...")
+                cd = 2 if fmt == "mxfp4" else 1
+                quant = quantise_mxfp4 if fmt == "mxfp4" else quantise_mxfp8
+                ex = {k + sfx: np.empty((experts[k].shape[0], experts[k].shape[1], experts[k].shape[2] // div), np.uint8)
+                      for k in ("gate", "up", "down") for sfx, div in (("_q", cd), ("_s", 32))}
 
                 def q(e):
                     for k in ("gate", "up", "down"):
-                        ex[k + "_q"][e], ex[k + "_s"][e] = quantise_mxfp4(experts[k][e])
+                        ex[k + "_q"][e], ex[k + "_s"][e] = quant(experts[k][e])
                 with ThreadPoolExecutor(16) as pool:
-                    list(pool.map(q, range(p.E)))
+                    list(pool.map(q, range(len(experts["gate"]))))
+                quantised[fmt] = ex
+            return quantised[fmt]
+        for name in ("prefill", "skewed", "mxfp4", "mxfp4_a8", "mxfp8", "mxfp8_a8"):
+            p = CONFIGS[name]
+            ex = experts if p.weight_format == "bf16" else encoded(p.weight_format)
             dp = upload(p, ex)
             log(f"measuring {name} T={p.T}")
             rp = measure(p, dp, max(5, args.steps // 3), 3, hip)
+            desc = {"skewed": ", clamp 4 / 7, clustered tokens, bias N(0,0.5)", "mxfp4": ", routed experts MXFP4",
+                    "mxfp8": ", routed experts MXFP8", "mxfp4_a8": ", routed experts MXFP4, MXFP8 activations",
+                    "mxfp8_a8": ", routed experts MXFP8, MXFP8 activations"}.get(name, "")
             line["secondary"][name] = {
-                "workload": f"{name}: T={p.T}, same layer" + (", clamp 4 / 7, clustered tokens, bias N(0,0.5)"
-                                                               if name == "skewed" else
-                                                               ", routed experts MXFP4" if name == "mxfp4" else ""),
+                "workload": f"{name}: T={p.T}, same layer{desc}",
                 "value": round(p.T / (rp["wall_ms"] * 1e-3), 1), "unit": "tokens/s",
                 "ms_per_step": round(rp["wall_ms"], 4),
                 "dtype": dtype_of(p),
                 "roofline": roofline(p, rp, measured=measured), "layer": layer_summary(p, rp, measured),
                 "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
             checks.append((p, {k: dp[k] for k in host}, rp["idx"]))
-            if p.weight_format == "mxfp4":
-                del ex
             del dp
             torch.cuda.empty_cache()
         line["prefill"] = line["secondary"]["prefill"]

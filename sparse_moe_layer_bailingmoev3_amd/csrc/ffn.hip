@@ -70,6 +70,8 @@ struct FfnArgs {
   const uint8_t* as;
   uint8_t* oq;
   uint8_t* os;
+  // the launch covers the tiles of experts e_lo .. e_hi-1 only (e_hi = 0: all E + S experts)
+  int e_lo, e_hi;
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -520,7 +522,7 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
       const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / VPB);
       const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
       wq[m][f] = base + row * (K / VPB) + q * 16;
-      wsc[m][f] = sbase + row * (K / 32) + q;
+      wsc[m][f] = sbase + row * (K / 32);
     }
 
   struct WSt {
@@ -563,7 +565,10 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
         const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (KS / VPB);
 #pragma unroll
         for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + 64 * r);
-        st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32)];
+        // the step's four block scales of the row in one aligned word (K / 32 is a multiple of
+        // 4); the lane's byte is taken where the MFMA uses it.  (A byte load here made the
+        // compiler zero-extend it at the loop latch, which waited for every load in flight.)
+        st.sc[m][f] = *(const uint32_t*)(wsc[m][f] + (size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32));
       }
   };
   // the token fragment of mf: row r16's codes 16q .. 16q+15 and 64+16q .. 64+16q+15, and the
@@ -600,7 +605,8 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
 #pragma unroll
         for (int f = 0; f < RF; ++f)
           acc[m][f][mf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[m][f], bf[mf & 1], acc[m][f][mf], AFMT, 0, 0, (int)st.sc[m][f], 0, bs[mf & 1]);
+              af[m][f], bf[mf & 1], acc[m][f][mf], AFMT, 0, 0, (int)((st.sc[m][f] >> (8 * q)) & 0xFFu), 0,
+              bs[mf & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -715,7 +721,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr bool PADDED = FMT != FMT_BF16 || MF >= 4;
   constexpr int BM = MF * 16;
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
-  __shared__ __align__(16) uint16_t lds[2 * NTP * BM * (KS + 16)];
+  // bf16 token planes (double-buffered, rows padded by 32 bytes), or for MXFP8 activations
+  // the codes (rows padded by 16 bytes) and scale words of two steps
+  constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? 2 * BM * (128 + 16) + 2 * BM * 4 : 2 * NTP * BM * (KS + 16) * 2;
+  __shared__ __align__(16) uint8_t lds_raw[LDS_BYTES];
+  uint16_t* lds = (uint16_t*)lds_raw;
 
   // device work list: work id -> (tile, sub-tile, row-block group); consecutive work ids
   // run on the same XCD.  A tile of the list holds bm_list positions and splits into
@@ -724,7 +734,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   // L2); group-major order, for a single weight set, the tiles of a row-block group (they
   // share its weight rows).
   const int subs = a.bm_list / BM;
-  const int ntsub = (a.dense ? (a.T + a.bm_list - 1) / a.bm_list : a.tile_prefix[a.E + a.S]) * subs;
+  const int t_lo = a.dense || a.e_hi == 0 ? 0 : a.tile_prefix[a.e_lo];
+  const int t_hi = a.dense ? (a.T + a.bm_list - 1) / a.bm_list : a.tile_prefix[a.e_hi == 0 ? a.E + a.S : a.e_hi];
+  const int ntsub = (t_hi - t_lo) * subs;
   const int total = ntsub * a.ngroups * a.ksplit;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
@@ -741,7 +753,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
     tsub = w / a.ngroups;
     grp = w - tsub * a.ngroups;
   }
-  const int tile = tsub / subs, sub = tsub - tile * subs;
+  const int tile = t_lo + tsub / subs, sub = tsub - (tsub / subs) * subs;
   const int rb0 = grp * a.rbw, nrb_here = min(a.rbw, a.nrb - rb0);
   const int4 info = a.dense ? int4{0, tile * a.bm_list, min(a.bm_list, a.T - tile * a.bm_list), 0}
                             : ((const int4*)(a.tile_prefix + tile_info_offset(a.E)))[tile];
@@ -749,15 +761,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   if (m0 >= info.z) return;
   const int nrows = min(BM, info.z - m0);
   if constexpr (FMT != FMT_BF16 && ACT == ACT_MXFP8) {
-    if (e < a.E) {  // routed experts: MXFP8 activations on the scaled MFMA
-      ffn_tile_a8<NW, RF, MF, D, MODE, FMT>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
-      return;
-    }
+    // routed experts only (the shared expert runs in a bf16 launch of its own, so this kernel
+    // carries no bf16 registers): MXFP8 activations on the scaled MFMA
+    if (e < a.E) ffn_tile_a8<NW, RF, MF, D, MODE, FMT>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
+    return;
   } else if constexpr (FMT != FMT_BF16) {
-    if (e < a.E) {  // routed experts in the block format; the shared expert is bf16
-      ffn_tile<NW, RF, MF, D, MODE, KS, FMT, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
-      return;
-    }
+    // routed experts in the block format (the bf16 shared expert runs in launches of its own)
+    if (e < a.E) ffn_tile<NW, RF, MF, D, MODE, KS, FMT, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
+    return;
   }
   ffn_tile<NW, RF, MF, D, MODE, KS, FMT_BF16, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
 }
@@ -832,7 +843,7 @@ template <int MF, int FMT, int MODE, int ACT = ACT_BF16> struct FfnCfg {
 };
 
 template <int MF, int MODE, int FMT, int ACT = ACT_BF16>
-hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Tracer* tr) {
+hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Tracer* tr, const char* name = nullptr) {
   using C = FfnCfg<MF, FMT, MODE, ACT>;
   if (ACT == ACT_MXFP8 && (a.ksplit != 1 || a.dense)) return hipErrorInvalidValue;
   constexpr int ROWS = C::NW * C::RF * 16;  // weight rows per block of each matrix
@@ -856,20 +867,20 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   else
     return hipErrorInvalidValue;
   hipError_t err = hipGetLastError();
-  if (tr) tr->mark(MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
+  if (tr) tr->mark(name ? name : MODE == MODE_GATEUP ? "expert_gate_up" : "expert_down", s);
   return err;
 }
 
 template <int MODE>
 hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_tiles, hipStream_t s, Tracer* tr,
-                       int act = ACT_BF16) {
+                       int act = ACT_BF16, const char* name = nullptr) {
   if (act == ACT_MXFP8) {
 #define MOE_A8(F)                                                                    \
   switch (mf) {                                                                      \
-    case 1: return launch_one<1, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
-    case 2: return launch_one<2, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
-    case 4: return launch_one<4, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
-    case 8: return launch_one<8, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr);     \
+    case 1: return launch_one<1, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr, name);     \
+    case 2: return launch_one<2, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr, name);     \
+    case 4: return launch_one<4, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr, name);     \
+    case 8: return launch_one<8, MODE, F, ACT_MXFP8>(a, rbw, max_tiles, s, tr, name);     \
     default: return hipErrorInvalidValue;                                            \
   }
     if (fmt == FMT_MXFP4) MOE_A8(FMT_MXFP4)
@@ -896,11 +907,11 @@ hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_t
     }
   }
   switch (mf) {
-    case 1: return launch_one<1, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr);
-    case 2: return launch_one<2, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr);
-    case 4: return launch_one<4, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr);
-    case 8: return launch_one<8, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr);
-    default: return launch_one<16, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr);
+    case 1: return launch_one<1, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr, name);
+    case 2: return launch_one<2, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr, name);
+    case 4: return launch_one<4, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr, name);
+    case 8: return launch_one<8, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr, name);
+    default: return launch_one<16, MODE, FMT_BF16>(a, rbw, max_tiles, s, tr, name);
   }
 }
 
@@ -1014,14 +1025,37 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
 
   gu.bm_list = dn.bm_list = p.bm;
   gu.group_major = dn.group_major = p.group_major ? 1 : 0;
+  if (w.fmt == FMT_BF16) {  // bf16 weights: the shared expert is one more expert of the same launches
+    err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr);
+    if (err != hipSuccess) return err;
+    return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr);
+  }
+  // block-format weights: the routed experts on the MX kernels (with MXFP8 activations, the
+  // scaled-MFMA ones), the shared expert (bf16 weights and activations) on the bf16 kernels,
+  // each launch restricted to its experts' tiles; the MX kernels then carry no bf16 registers
   const int act = a8 ? ACT_MXFP8 : ACT_BF16;
+  FfnArgs gu_s = gu, dn_s = dn;
   if (a8) {
     gu.aq = ab->xq; gu.as = ab->xs; gu.oq = ab->hq; gu.os = ab->hs;
     dn.aq = ab->hq; dn.as = ab->hs;
   }
-  err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles, s, tr, act);
+  gu.e_lo = dn.e_lo = 0;
+  gu.e_hi = dn.e_hi = E;
+  gu_s.e_lo = dn_s.e_lo = E;
+  gu_s.e_hi = dn_s.e_hi = E + S;
+  const int64_t sh_tiles = S ? ((int64_t)T + p.bm - 1) / p.bm : 0;
+  err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess) return err;
-  return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr, act);
+  // the shared expert alone has few token tiles: one row block per workgroup spreads it over
+  // the chip
+  if (S) {
+    err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu_s, 1, FMT_BF16, sh_tiles, s, tr, ACT_BF16,
+                                   "expert_gate_up_shared");
+    if (err != hipSuccess) return err;
+  }
+  err = launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
+  if (err != hipSuccess || !S) return err;
+  return launch_mode<MODE_DOWN>(p.mf_down, dn_s, 1, FMT_BF16, sh_tiles, s, tr, ACT_BF16, "expert_down_shared");
 }
 
 hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales, hipStream_t s) {
