@@ -461,29 +461,34 @@ __device__ __forceinline__ void a8_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int NW, int RF, int MF, int D, int MODE, int WF>
+// KS = 128 * KC values per step: the KC 128-value chunks of a step are loaded together, so each
+// weight row is fetched in runs of 64 * KC (E2M1) or 128 * KC (E4M3) bytes; each chunk is one
+// scaled MFMA per (row block, token fragment).
+template <int NW, int RF, int MF, int D, int MODE, int WF, int KS>
 __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                             uint8_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
   constexpr int BM = MF * 16;
-  constexpr int KS = 128;
+  constexpr int KC = KS / 128;                     // 128-value chunks per step
   constexpr int NST = D + 1;                       // LDS token stages: D in flight + the one read
-  constexpr int SROWS = BM < 64 ? 64 : BM;         // scale words per stage (a dword load covers 64 rows)
-  constexpr int STAGE = BM * KS + SROWS * 4;
+  constexpr int SROWS = BM < 64 ? 64 : BM;         // rows per scale plane (a dword load covers 64 rows)
+  constexpr int STAGE = BM * KS + KC * SROWS * 4;  // codes, then one plane of scale words per chunk
   constexpr int ROWS = NW * RF * 16;
   constexpr bool FP4 = WF == FMT_MXFP4;
-  constexpr int WREGS = FP4 ? 1 : 2;
+  constexpr int WREGS = FP4 ? 1 : 2;               // 16-byte weight loads per (row block, chunk)
   constexpr int VPB = FP4 ? 2 : 1;                 // weight values per byte
   constexpr int AFMT = FP4 ? 4 : 0;                // scaled-MFMA operand format: 4 = E2M1, 0 = E4M3
-  // token loads per step: 1 KB (8 rows) of codes per wave instruction, 64 scale words per
-  // dword instruction; every wave issues the same number (small tiles repeat an instruction
-  // in a second wave, writing the same bytes), so that one wait count covers every wave
-  constexpr int CODE_INSTR = BM / 8, SCALE_INSTR = SROWS / 64;
+  // token loads per step: 1 KB of codes per wave instruction, 64 scale words (one chunk) per
+  // dword instruction; every wave issues the same number (small tiles repeat an instruction in
+  // a second wave, writing the same bytes), so that one wait count covers every wave
+  constexpr int RPI = 1024 / KS;                   // code rows per instruction
+  constexpr int CODE_INSTR = BM / RPI, SCALE_INSTR = KC * (SROWS / 64);
   constexpr int NCI = (CODE_INSTR + NW - 1) / NW, NSI = (SCALE_INSTR + NW - 1) / NW;
-  constexpr int NLOAD = NCI + NSI + NMAT * RF * (WREGS + 1);  // loads per wave per step
+  constexpr int NLOAD = NCI + NSI + NMAT * RF * (KC * WREGS + 1);  // loads per wave per step
   constexpr int VM_WAIT = (D - 1) * NLOAD;
   static_assert(MODE == MODE_DOWN || RF % 2 == 0, "h is rounded in 32-row blocks: two fragments per wave");
-  static_assert(BM % 8 == 0 && KS == 128, "token rows are 8 x 16-byte chunks");
+  static_assert((KC == 1 || KC == 2) && BM % RPI == 0, "steps of 128 or 256 values");
+  static_assert(VM_WAIT < 64, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -504,40 +509,43 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     ok = r < nrows;
     return pos0 + pr;
   };
-  // codes: instruction i covers tile rows 8i .. 8i+7; lane l writes row 8i + l/8, LDS slot
-  // l%8, which holds chunk (l%8) ^ (row & 7) of the row (the XOR keeps the fragment reads of
-  // 8 consecutive rows on distinct banks)
+  // codes: a row is KS / 16 chunks of 16 bytes; within each 128-byte segment chunk c sits in
+  // slot c ^ (row & 7) (so the fragment reads of 8 consecutive rows fall on distinct banks).
+  // Instruction i covers rows RPI*i .. RPI*i + RPI-1; lane l writes row RPI*i + l / (KS/16),
+  // slot l % (KS/16), and so loads the chunk that slot holds.
   const uint8_t* csrc[NCI];
   int cdst[NCI];
 #pragma unroll
   for (int k = 0; k < NCI; ++k) {
     const int ci = (wave + k * NW) % CODE_INSTR;
-    const int r = ci * 8 + (lane >> 3);
+    const int r = ci * RPI + lane / (KS / 16), slot = lane % (KS / 16);
     bool ok;
     const int64_t row = row_src(r, ok);
-    csrc[k] = a.aq + row * K + 16 * ((lane & 7) ^ (r & 7));
+    csrc[k] = a.aq + row * K + (slot >> 3) * 128 + 16 * ((slot & 7) ^ (r & 7));
     cdst[k] = ci * 1024;
   }
+  // scales: plane c holds, per row, the dword of the step's chunk c (its four block scales)
   const uint8_t* ssrc[NSI];
   int sdst[NSI];
 #pragma unroll
   for (int k = 0; k < NSI; ++k) {
     const int si = (wave + k * NW) % SCALE_INSTR;
-    const int r = si * 64 + lane;
+    const int c = si % KC, r = (si / KC) * 64 + lane;
     bool ok;
     const int64_t row = row_src(r < BM ? r : 0, ok);
-    ssrc[k] = a.as + row * (K / 32);
-    sdst[k] = BM * KS + si * 256;
+    ssrc[k] = a.as + row * (K / 32) + 4 * c;
+    sdst[k] = BM * KS + c * SROWS * 4 + (si / KC) * 256;
   }
   // the epilogue's row validity (gate/up: a position without a token gets h = 0)
   bool row_ok[MF];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf) row_src(mf * 16 + r16, row_ok[mf]);
 
-  // weights: lane group q gives the scale of block q; E2M1 codes: block q's 16 bytes; E4M3
-  // codes: bytes 16q .. 16q+15 and 64+16q .. 64+16q+15 of the step (the instruction's layout).
-  // Buffer loads: one resource per matrix of this expert, the lane's row in a VGPR offset
-  // and the step in an SGPR offset, so a step's loads need no address arithmetic per lane.
+  // weights: lane group q gives the scale of block q of a chunk; E2M1 codes: block q's 16
+  // bytes; E4M3 codes: bytes 16q .. 16q+15 and 64+16q .. 64+16q+15 of the chunk (the
+  // instruction's layout).  Buffer loads: one resource per matrix of this expert, the lane's
+  // row in a VGPR offset and the step in an SGPR offset, so a step's loads need no address
+  // arithmetic per lane.
   const int nbase = rb0 * ROWS + wave * RF * 16;
   __amdgpu_buffer_rsrc_t wres[NMAT], sres[NMAT];
 #pragma unroll
@@ -556,10 +564,10 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
   }
 
   // a weight stage holds the MFMA a operands themselves (an E2M1 operand's upper half stays
-  // zero) and the rows' scale words of the step
+  // zero) and the rows' scale words of each chunk
   struct WSt {
-    i32x8 w[NMAT][RF];
-    uint32_t sc[NMAT][RF];
+    i32x8 w[NMAT][RF][KC];
+    uint32_t sc[NMAT][RF][KC];
   };
   floatx4 acc[NMAT][RF][MF];
 #pragma unroll
@@ -587,7 +595,7 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
 #pragma unroll
     for (int k = 0; k < NCI; ++k) a8_dma16(csrc[k] + i_ks * KS, st + cdst[k]);
 #pragma unroll
-    for (int k = 0; k < NSI; ++k) a8_dma4(ssrc[k] + i_ks * 4, st + sdst[k]);
+    for (int k = 0; k < NSI; ++k) a8_dma4(ssrc[k] + i_ks * (KS / 32), st + sdst[k]);
   };
   auto issue_w = [&](WSt& w) {
     const int wso = i_rb * ROWS * (K / VPB) + i_ks * (KS / VPB);
@@ -596,58 +604,72 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
-        const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f], wso, 0));
-        w.w[m][f][0] = (int)lo[0];
-        w.w[m][f][1] = (int)lo[1];
-        w.w[m][f][2] = (int)lo[2];
-        w.w[m][f][3] = (int)lo[3];
-        if constexpr (!FP4) {
-          const u32x4 hi =
-              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + 64, wso, 0));
-          w.w[m][f][4] = (int)hi[0];
-          w.w[m][f][5] = (int)hi[1];
-          w.w[m][f][6] = (int)hi[2];
-          w.w[m][f][7] = (int)hi[3];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const u32x4 lo = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * (128 / VPB), wso, 0));
+          w.w[m][f][c][0] = (int)lo[0];
+          w.w[m][f][c][1] = (int)lo[1];
+          w.w[m][f][c][2] = (int)lo[2];
+          w.w[m][f][c][3] = (int)lo[3];
+          if constexpr (!FP4) {
+            const u32x4 hi = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * 128 + 64, wso, 0));
+            w.w[m][f][c][4] = (int)hi[0];
+            w.w[m][f][c][5] = (int)hi[1];
+            w.w[m][f][c][6] = (int)hi[2];
+            w.w[m][f][c][7] = (int)hi[3];
+          }
         }
-        // the step's four block scales of the row in one aligned word (K / 32 is a multiple
-        // of 4); the lane's byte is shifted down where the MFMA uses it
-        w.sc[m][f] = __builtin_amdgcn_raw_buffer_load_b32(sres[m], soff[f], sso, 0);
+        // the row's block scales of the step, one word per chunk (K / 32 is a multiple of 4 * KC
+        // bytes); the lane's byte is shifted down where the MFMA uses it
+        if constexpr (KC == 2) {
+          const auto sw = __builtin_amdgcn_raw_buffer_load_b64(sres[m], soff[f], sso, 0);
+          w.sc[m][f][0] = (uint32_t)sw[0];
+          w.sc[m][f][KC - 1] = (uint32_t)sw[1];
+        } else {
+          w.sc[m][f][0] = __builtin_amdgcn_raw_buffer_load_b32(sres[m], soff[f], sso, 0);
+        }
       }
   };
-  // the token fragment of mf in stage `st`: row r16's codes 16q .. 16q+15 (chunk q) and
-  // 64+16q .. 64+16q+15 (chunk 4+q), read through the chunk swizzle, and block q's scale
-  auto bfrag = [&](const uint8_t* st, int mf) {
+  // the token fragment of (mf, chunk c) in stage `st`: row r16's codes 16q .. 16q+15 and
+  // 64+16q .. 64+16q+15 of the chunk, read through the slot swizzle, and block q's scale (the
+  // instruction reads byte 0 of a scale register: the lane's byte is shifted down, the bytes
+  // above it are ignored)
+  auto bfrag = [&](const uint8_t* st, int mf, int c) {
     const int r = mf * 16 + r16;
-    const uint8_t* L = st + r * KS;
+    const uint8_t* L = st + r * KS + c * 128;
     const u32x4 lo = *(const u32x4*)(L + 16 * (q ^ (r & 7)));
     const u32x4 hi = *(const u32x4*)(L + 16 * ((4 + q) ^ (r & 7)));
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  // (the instruction reads byte 0 of a scale register: the lane's byte is shifted down, the
-  // bytes above it are ignored)
-  auto bscale = [&](const uint8_t* st, int mf) {
-    return (int)(((const uint32_t*)(st + BM * KS))[mf * 16 + r16] >> (8 * q));
+  auto bscale = [&](const uint8_t* st, int mf, int c) {
+    return (int)(((const uint32_t*)(st + BM * KS + c * SROWS * 4))[mf * 16 + r16] >> (8 * q));
   };
   auto compute = [&](const WSt& w, int step) {
     const uint8_t* st = lds + (step % NST) * STAGE;
-    i32x8 bf[2];
-    int bs[2];
-    bf[0] = bfrag(st, 0);
-    bs[0] = bscale(st, 0);
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      if (mf + 1 < MF) {  // the next fragment's LDS reads overlap this one's MFMAs
-        bf[(mf + 1) & 1] = bfrag(st, mf + 1);
-        bs[(mf + 1) & 1] = bscale(st, mf + 1);
+    for (int c = 0; c < KC; ++c) {
+      i32x8 bf[2];
+      int bs[2];
+      bf[0] = bfrag(st, 0, c);
+      bs[0] = bscale(st, 0, c);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        if (mf + 1 < MF) {  // the next fragment's LDS reads overlap this one's MFMAs
+          bf[(mf + 1) & 1] = bfrag(st, mf + 1, c);
+          bs[(mf + 1) & 1] = bscale(st, mf + 1, c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int f = 0; f < RF; ++f)
+            acc[m][f][mf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                w.w[m][f][c], bf[mf & 1], acc[m][f][mf], AFMT, 0, 0, (int)(w.sc[m][f][c] >> (8 * q)), 0,
+                bs[mf & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int f = 0; f < RF; ++f)
-          acc[m][f][mf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              w.w[m][f], bf[mf & 1], acc[m][f][mf], AFMT, 0, 0, (int)(w.sc[m][f] >> (8 * q)), 0, bs[mf & 1]);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -709,7 +731,9 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int f = 0; f < RF; ++f) ws[j].w[m][f] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) ws[j].w[m][f][c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     issue_t(j);
@@ -783,7 +807,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
   // bf16 token planes (double-buffered, rows padded by 32 bytes), or for MXFP8 activations a
   // ring of D + 1 stages of codes and scale words
-  constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? (D + 1) * (BM * 128 + (BM < 64 ? 64 : BM) * 4)
+  constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? (D + 1) * (BM * KS + (KS / 128) * (BM < 64 ? 64 : BM) * 4)
                                              : 2 * NTP * BM * (KS + 16) * 2;
   __shared__ __align__(16) uint8_t lds_raw[LDS_BYTES];
   uint16_t* lds = (uint16_t*)lds_raw;
@@ -824,7 +848,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   if constexpr (FMT != FMT_BF16 && ACT == ACT_MXFP8) {
     // routed experts only (the shared expert runs in a bf16 launch of its own, so this kernel
     // carries no bf16 registers): MXFP8 activations on the scaled MFMA
-    if (e < a.E) ffn_tile_a8<NW, RF, MF, D, MODE, FMT>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
+    if (e < a.E) ffn_tile_a8<NW, RF, MF, D, MODE, FMT, KS>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
     return;
   } else if constexpr (FMT != FMT_BF16) {
     // routed experts in the block format (the bf16 shared expert runs in launches of its own)
@@ -893,17 +917,17 @@ template <int MF, int FMT, int MODE, int ACT = ACT_BF16> struct FfnCfg {
   static constexpr bool WIDE = !FP4 && (MF == 1 || (MF == 2 && !DOWN));
   static constexpr int NW = (MF <= 2 || DOWN || A8) ? 4 : 8;
   static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN || A8) ? 2 : 1;
-  static constexpr int KS = FP4 ? 128 : WIDE ? ((MF == 1 && DOWN) ? 384 : 256) : 64;
-  // MXFP8 activations: tokens in an LDS ring (no registers), weights D steps ahead in registers
-  // (2, 3 and 4 measured within 2 % of each other at T = 4096)
-  static constexpr int D = A8 ? 3
+  static constexpr int KS = A8 ? 256 : FP4 ? 128 : WIDE ? ((MF == 1 && DOWN) ? 384 : 256) : 64;
+  // MXFP8 activations: 256-value steps where K allows (128 otherwise), tokens in an LDS ring
+  // (no registers), weights D steps ahead in registers
+  static constexpr int D = A8 ? 2
                          : WIDE ? 2
                          : MF <= 2 ? (FP4 ? 3 : 4)
                          : MF == 4 ? (FP4 ? 2 : 4)
                          : MF == 8 ? (FP4 ? 2 : (DOWN ? 3 : 4))
                                    : 2;
   static constexpr int KS_MID = WIDE ? 256 : KS;  // where K is not a multiple of KS
-  static constexpr int KS_ALT = WIDE ? 128 : KS, D_ALT = WIDE ? 4 : D;
+  static constexpr int KS_ALT = (WIDE || A8) ? 128 : KS, D_ALT = WIDE ? 4 : D;
 };
 
 template <int MF, int MODE, int FMT, int ACT = ACT_BF16>
@@ -925,7 +949,7 @@ hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Trac
   else if (ACT == ACT_BF16 && C::KS_MID != C::KS && kspan % C::KS_MID == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D, MODE, FMT, C::KS_MID, ACT>, dim3((unsigned)grid),
            dim3(C::NW * 64), s, a);
-  else if (ACT == ACT_BF16 && C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
+  else if (C::KS_ALT != C::KS && kspan % C::KS_ALT == 0)
     launch(tr, ffn_kernel<C::NW, C::RF, MF, C::D_ALT, MODE, FMT, C::KS_ALT, ACT>, dim3((unsigned)grid),
            dim3(C::NW * 64), s, a);
   else
