@@ -58,8 +58,10 @@ struct FfnArgs {
   int ngroups;                  // ceil(nrb / rbw): row-block groups per tile
   int bm_list;                  // positions per tile of the device tile list (a multiple of 16*MF)
   int group_major;              // 1: work id = group * tiles + tile (else tile * groups + group)
-  int dense;                    // 1: one weight set and the identity permutation (a dense FFN): tiles
-                                // follow from T, no dispatch arrays are read, down writes bf16 out [T,N]
+  int dense;                    // 1: one weight set and the identity permutation (a dense FFN, or the
+                                // shared expert of a block-format layer): tiles follow from T, no
+                                // dispatch arrays are read
+  int out_bf16;                 // down writes bf16 out [T,N] (the dense FFN) instead of fp32 y
   int ksplit;                   // workgroups splitting the reduction (down of a dense FFN; else 1)
   float* part;                  // ksplit > 1: fp32 partial sums [ksplit,T,N], added in order later
   float limit, shared_limit;
@@ -368,7 +370,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
             *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
           } else if (a.ksplit > 1) {
             *(floatx4*)(a.part + ((size_t)ksp * a.T + pos0 + j) * N + ncol + f * 16) = acc[0][f][mf];
-          } else if (a.dense) {
+          } else if (a.out_bf16) {
             const floatx4 v = acc[0][f][mf];
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
@@ -471,7 +473,7 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
   constexpr int BM = MF * 16;
   constexpr int KC = KS / 128;                     // 128-value chunks per step
   constexpr int NST = D + 1;                       // LDS token stages: D in flight + the one read
-  constexpr int SROWS = BM < 64 ? 64 : BM;         // rows per scale plane (a dword load covers 64 rows)
+  constexpr int SROWS = (BM + 63) / 64 * 64;       // rows per scale plane (a dword load covers 64 rows)
   constexpr int STAGE = BM * KS + KC * SROWS * 4;  // codes, then one plane of scale words per chunk
   constexpr int ROWS = NW * RF * 16;
   constexpr bool FP4 = WF == FMT_MXFP4;
@@ -800,6 +802,26 @@ __global__ __launch_bounds__(256) void mx8_quant_kernel(const uint16_t* __restri
   scales[i] = (uint8_t)sb;
 }
 
+// A tile of block-format experts runs as ceil(nrows / 16) fragments of 16 positions: the
+// fragments past its last token issue no loads, LDS reads or MFMAs, so an expert with n tokens
+// costs ceil(n / 16) fragments rather than whole tiles (at 4096 tokens, 64-position tiles are
+// 65 % occupied by tokens, their 16-position fragments 90 %).  Bf16 activations take the
+// decoding kernel, MXFP8 activations the scaled MFMA.
+template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS, int ACT, bool PADDED>
+__device__ __forceinline__ void ffn_tile_mx(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
+                                            int ksp, uint16_t* lds) {
+  if constexpr (MF > 1) {
+    if (nrows <= (MF - 1) * 16) {
+      ffn_tile_mx<NW, RF, MF - 1, D, MODE, FMT, KS, ACT, PADDED>(a, e, pos0, nrows, rb0, nrb_here, ksp, lds);
+      return;
+    }
+  }
+  if constexpr (ACT == ACT_MXFP8)
+    ffn_tile_a8<NW, RF, MF, D, MODE, FMT, KS>(a, e, pos0, nrows, rb0, nrb_here, (uint8_t*)lds);
+  else
+    ffn_tile<NW, RF, MF, D, MODE, KS, FMT, PADDED>(a, e, pos0, nrows, rb0, nrb_here, ksp, lds);
+}
+
 template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS, int ACT>
 __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr bool PADDED = FMT != FMT_BF16 || MF >= 4;
@@ -807,7 +829,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
   // bf16 token planes (double-buffered, rows padded by 32 bytes), or for MXFP8 activations a
   // ring of D + 1 stages of codes and scale words
-  constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? (D + 1) * (BM * KS + (KS / 128) * (BM < 64 ? 64 : BM) * 4)
+  constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? (D + 1) * (BM * KS + (KS / 128) * ((BM + 63) / 64 * 64) * 4)
                                              : 2 * NTP * BM * (KS + 16) * 2;
   __shared__ __align__(16) uint8_t lds_raw[LDS_BYTES];
   uint16_t* lds = (uint16_t*)lds_raw;
@@ -845,14 +867,10 @@ __global__ __launch_bounds__(NW * 64) void ffn_kernel(FfnArgs a) {
   const int e = info.x, m0 = sub * BM;
   if (m0 >= info.z) return;
   const int nrows = min(BM, info.z - m0);
-  if constexpr (FMT != FMT_BF16 && ACT == ACT_MXFP8) {
-    // routed experts only (the shared expert runs in a bf16 launch of its own, so this kernel
-    // carries no bf16 registers): MXFP8 activations on the scaled MFMA
-    if (e < a.E) ffn_tile_a8<NW, RF, MF, D, MODE, FMT, KS>(a, e, info.y + m0, nrows, rb0, nrb_here, (uint8_t*)lds);
-    return;
-  } else if constexpr (FMT != FMT_BF16) {
-    // routed experts in the block format (the bf16 shared expert runs in launches of its own)
-    if (e < a.E) ffn_tile<NW, RF, MF, D, MODE, KS, FMT, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
+  if constexpr (FMT != FMT_BF16) {
+    // routed experts in the block format only (the bf16 shared expert runs in launches of its
+    // own, so these kernels carry no bf16-weight registers)
+    if (e < a.E) ffn_tile_mx<NW, RF, MF, D, MODE, FMT, KS, ACT, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
     return;
   }
   ffn_tile<NW, RF, MF, D, MODE, KS, FMT_BF16, PADDED>(a, e, info.y + m0, nrows, rb0, nrb_here, ksp, lds);
@@ -1005,8 +1023,22 @@ hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_t
 
 }  // namespace
 
+// The shared expert of a block-format layer runs as a dense FFN over all T tokens (one bf16
+// weight set): tiles of 16 * mf tokens growing with T, the tiles of a row block side by side
+// up to 512 tokens (measured at 4096 tokens, hidden 2560, intermediate 768: 128-token tiles
+// take 0.067 ms for gate/up, 64-token tiles 0.101 ms)
+SharedPlan shared_plan(int64_t T) {
+  SharedPlan sp;
+  sp.mf = T <= 32 ? 1 : T <= 128 ? 2 : T <= 512 ? 4 : 8;
+  sp.mf_down = std::min(sp.mf, 4);
+  sp.group_major = T <= 512 ? 1 : 0;
+  sp.tiles = (T + 16 * sp.mf - 1) / (16 * sp.mf);
+  return sp;
+}
+
 FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   FfnPlan p;
+  p.topk = K;
   const double avg = (double)T * K / E;  // routed tokens per expert on average
   // tile list of 16*mf positions; gate/up runs whole tiles, down runs sub-tiles of 16*mf_down
   // (measured: the down GEMM, which reads two h planes, is fastest with 64-token tiles at
@@ -1119,8 +1151,10 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
     return launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles, s, tr);
   }
   // block-format weights: the routed experts on the MX kernels (with MXFP8 activations, the
-  // scaled-MFMA ones), the shared expert (bf16 weights and activations) on the bf16 kernels,
-  // each launch restricted to its experts' tiles; the MX kernels then carry no bf16 registers
+  // scaled-MFMA ones), restricted to their tiles, so that they carry no bf16-weight registers;
+  // the shared expert (bf16 weights and activations) on the bf16 kernels as a dense FFN over
+  // all T tokens, whose block of sorted positions is the identity at T*K (so its tile size
+  // follows from T, not from the routed experts' tokens)
   const int act = a8 ? ACT_MXFP8 : ACT_BF16;
   FfnArgs gu_s = gu, dn_s = dn;
   if (a8) {
@@ -1129,21 +1163,28 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   }
   gu.e_lo = dn.e_lo = 0;
   gu.e_hi = dn.e_hi = E;
-  gu_s.e_lo = dn_s.e_lo = E;
-  gu_s.e_hi = dn_s.e_hi = E + S;
   const int64_t sh_tiles = S ? ((int64_t)T + p.bm - 1) / p.bm : 0;
   err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess) return err;
-  // the shared expert alone has few token tiles: one row block per workgroup spreads it over
-  // the chip
+  const SharedPlan sp = shared_plan(T);
+  const size_t pos = (size_t)T * (size_t)p.topk;  // the shared expert's first sorted position
   if (S) {
-    err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu_s, 1, FMT_BF16, sh_tiles, s, tr, ACT_BF16,
-                                   "expert_gate_up_shared");
+    gu_s.act = x; gu_s.sorted_token = nullptr; gu_s.offsets = nullptr; gu_s.tile_prefix = nullptr;
+    gu_s.w0 = w.sh_gate; gu_s.w1 = w.sh_up; gu_s.s0 = gu_s.s1 = nullptr;
+    gu_s.out = h_hi + pos * I; gu_s.out_lo = h_lo + pos * I;
+    gu_s.E = 1; gu_s.S = 0; gu_s.limit = shared_limit;
+    gu_s.dense = 1; gu_s.bm_list = 16 * sp.mf; gu_s.group_major = sp.group_major;
+    err = launch_mode<MODE_GATEUP>(sp.mf, gu_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_gate_up_shared");
     if (err != hipSuccess) return err;
   }
   err = launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess || !S) return err;
-  return launch_mode<MODE_DOWN>(p.mf_down, dn_s, 1, FMT_BF16, sh_tiles, s, tr, ACT_BF16, "expert_down_shared");
+  dn_s.act = h_hi + pos * I; dn_s.act_lo = h_lo + pos * I;
+  dn_s.w0 = w.sh_down; dn_s.s0 = nullptr;
+  dn_s.out = y + pos * H;
+  dn_s.E = 1; dn_s.S = 0; dn_s.limit = shared_limit;
+  dn_s.dense = 1; dn_s.out_bf16 = 0; dn_s.bm_list = 16 * sp.mf; dn_s.group_major = sp.group_major;
+  return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_down_shared");
 }
 
 hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales, hipStream_t s) {
@@ -1171,6 +1212,7 @@ hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uin
   FfnArgs dn = gu;
   dn.act = h_hi; dn.act_lo = h_lo; dn.out_lo = nullptr; dn.w0 = down; dn.w1 = nullptr; dn.out = out;
   dn.K = I; dn.N = H;
+  dn.out_bf16 = 1;
   dn.ksplit = p.ksplit_down;
   dn.part = part;
   const int64_t ntiles = ((int64_t)T + p.bm - 1) / p.bm;

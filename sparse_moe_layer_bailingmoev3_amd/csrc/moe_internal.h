@@ -121,8 +121,16 @@ struct FfnPlan {
   bool group_major;  // work order: the tiles of one row-block group consecutive (one weight set)
   int ksplit_down;   // workgroups splitting the down reduction (a dense FFN with few tokens; else 1)
   int64_t max_tiles;
+  int topk;          // routed slots per token (the shared expert's positions start at T * topk)
 };
 FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I);
+// the shared expert's own launches in block-format layers (a dense FFN over the T tokens)
+struct SharedPlan {
+  int mf, mf_down;   // 16-token fragments per tile of gate/up and of down
+  int group_major;   // work order: the tiles of one row block consecutive
+  int64_t tiles;     // ceil(T / (16 * mf))
+};
+SharedPlan shared_plan(int64_t T);
 // MXFP8 activations of the routed experts (act == ACT_MXFP8): x rounded to MXFP8 (codes [T,H],
 // scales [T,H/32]) by a first kernel, h written by gate/up as MXFP8 (codes [P,I], scales
 // [P,I/32]); the shared expert keeps bf16 x and the two bf16 h planes
