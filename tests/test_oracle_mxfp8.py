@@ -167,3 +167,21 @@ def test_mxfp8_activation_error_on_the_mxfp4_layer():
           f"std(err)/RMS = {err.std() / rms:.4f}")
     assert err.max() / rms > 5e-2
     assert err.std() / rms < 5e-2
+
+
+def test_synthetic_weight_quantiser_matches_the_oracle():
+    """The MXFP8 expert weights of the block-format workloads come from synthetic's quantiser
+    (binade rounding with numpy's rint), written apart from the oracle's (nearest value on the
+    E4M3 grid).  Both follow the OCP MX v1.0 conversion, so on bf16 weights spanning many
+    binades, subnormal elements and saturating blocks they give the same codes and scales."""
+    from synthetic import f32_to_bf16_bits, quantise_mxfp8
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((48, 256)) * np.exp2(rng.integers(-30, 30, size=(48, 1)))
+    w[:, 1::32] *= 2.0 ** -14          # subnormal elements next to a block maximum
+    w[::5, ::3] = 0.0
+    w[7] = 0.0                         # all-zero blocks
+    bits = f32_to_bf16_bits(w.astype(np.float32))
+    codes, scales = quantise_mxfp8(bits)
+    want_c, want_s = oracle.mxfp8_quantise(oracle.bf16_to_f64(bits))
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(oracle.e4m3_value(codes), oracle.e4m3_value(want_c))
