@@ -446,6 +446,36 @@ def measured_peaks(hip, nbytes=1 << 30, n=4096):
                     "and torch bf16 matmul 4096^3 (hipBLASLt); best over grids and runs"}
 
 
+def layout_probe(hip, rows=225 * 1536, K=2560, reps=5):
+    """The decode gate/up weight stream alone (225 experts x 1536 rows x 2560 bf16, the decode
+    workload's touched experts) read by the probe kernel in the few-token kernel's pattern, from
+    the row-major layout and from a blocked one (each wave-step's 16 rows x 256 values
+    contiguous): what a blocked weight layout would buy the decode kernels."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(moe.lib_path()), "libmoe_probe.so"))
+    stream = torch.cuda.current_stream().cuda_stream
+    w = torch.empty(rows * K, dtype=torch.int16, device="cuda").random_(-32768, 32767)
+    sink = torch.zeros(rows // 64, dtype=torch.int32, device="cuda")
+    V, I = ctypes.c_void_p, ctypes.c_int
+    res = {}
+    for name, blocked in (("row_major_GBps", 0), ("blocked_GBps", 1)):
+        launch = lambda: lib.moe_probe_frag_read(V(w.data_ptr()), I(rows), I(K), I(blocked), V(sink.data_ptr()), V(stream))  # noqa: E731
+        assert launch() == 0
+        t = 1e9
+        for _ in range(reps):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            assert launch() == 0
+            hip.record(e1, stream)
+            t = min(t, hip.elapsed_ms(e0, e1))
+        res[name] = round(rows * K * 2 / (t * 1e-3) / 1e9, 1)
+    del w
+    torch.cuda.empty_cache()
+    res["bytes"] = rows * K * 2
+    return res
+
+
 def layer_summary(shape, r, measured=None):
     """Whole-layer figures: algorithmic bytes of the step and fractions of both peaks."""
     counts = r["counts"]
@@ -463,6 +493,53 @@ def layer_summary(shape, r, measured=None):
                 hbm_frac_of_measured_read=round(byts / (ms * 1e-3) / 1e9 / measured["read_GBps"], 4) if measured else None,
                 router_fp32_flops=2.0 * T * H * E, touched_experts=touched, step_ms_dist=r.get("step_dist"),
                 load=load_stats(shape, counts))
+
+
+def library_gemm(shape, d, idx, hip, reps=10):
+    """For comparison only (not part of the product): the same expert products as torch's
+    batched bf16 matmul (hipBLASLt on ROCm), with the tokens already gathered per expert and
+    every expert padded or cut to P positions, P = the mean tokens per expert rounded up to 16
+    (about the same flops as the routed work of the step; experts above P lose their extra
+    tokens).  gate and up are two products of [E,I,H] x [E,H,P] and down one of [E,H,I] x
+    [E,I,P]; weights as the left operand, so no transposed right operand reaches the batched
+    product."""
+    import torch
+    E, H, I, T, K = shape.E, shape.H, shape.I, shape.T, shape.K
+    P = int(np.ceil(T * K / E / 16) * 16)
+    gate, up, down = d["weights"]._keep[:3]
+    e = torch.from_numpy(idx.astype(np.int64).reshape(-1)).cuda()
+    tok = torch.arange(T, device="cuda").repeat_interleave(K)
+    order = torch.argsort(e, stable=True)
+    es, ts = e[order], tok[order]
+    cnt = torch.bincount(e, minlength=E)
+    rank = torch.arange(es.numel(), device="cuda") - (torch.cumsum(cnt, 0) - cnt)[es]
+    keep = rank < P
+    xp = torch.zeros((E, P, H), dtype=torch.bfloat16, device="cuda")
+    xp[es[keep], rank[keep]] = d["x"][ts[keep]]
+    xT = xp.transpose(1, 2).contiguous()                       # [E, H, P]
+    hT = torch.zeros((E, I, P), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [hip.event() for _ in range(reps + 1)]
+        hip.record(ev[0], stream)
+        for i in range(reps):
+            fn()
+            hip.record(ev[i + 1], stream)
+        torch.cuda.synchronize()
+        return float(np.median([hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(reps)]))
+
+    gu_ms = timed(lambda: (torch.bmm(gate, xT), torch.bmm(up, xT)))
+    dn_ms = timed(lambda: torch.bmm(down, hT))
+    flops_gu, flops_dn = 2.0 * E * P * 2 * I * H, 2.0 * E * P * H * I
+    del xp, xT, hT
+    torch.cuda.empty_cache()
+    return {"positions_per_expert": P, "gate_up_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
+            "gate_up_TFLOPs": round(flops_gu / gu_ms * 1e-9, 1), "down_TFLOPs": round(flops_dn / dn_ms * 1e-9, 1),
+            "note": "torch.bmm (hipBLASLt) on tokens gathered and padded to P per expert beforehand; "
+                    "comparison only, the gather, SwiGLU and combine are not in these times"}
 
 
 def routing_check(shape, d, idx_gpu):
@@ -671,6 +748,10 @@ def main():
                     help="token counts of the --dense measurement")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--layout-probe", action="store_true",
+                    help="also read the decode weight stream from the row-major and a blocked layout")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the expert products as torch's batched bf16 matmul (hipBLASLt), for comparison")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ from the rocprofv3 runs in DIR and exit")
     args = ap.parse_args()
     if args.summarize:
@@ -743,6 +824,10 @@ def main():
         "measured_peaks": measured,
         "expert_bias_update": time_bias_update(shape, r["counts"], hip),
     }
+    if args.layout_probe:
+        line["layout_probe"] = layout_probe(hip)
+    if args.library_gemm and shape.weight_format == "bf16":
+        line["library_gemm"] = library_gemm(shape, d, r["idx"], hip)
     host = ("x_bits", "router_w_np", "bias_np")
     checks = [(shape, {k: d[k] for k in host}, r["idx"])]
     if not args.no_secondary and shape.name == "decode":

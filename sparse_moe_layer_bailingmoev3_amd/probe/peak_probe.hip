@@ -68,6 +68,46 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* __rest
   if (s == -1234.5f) sink[blockIdx.x] = s;
 }
 
+// The weight stream of the few-token expert kernel, alone: each wave reads 16 rows of a
+// [rows, K] bf16 matrix in 256-value steps (8 loads of 16 bytes per lane, two steps in
+// flight), lane (r, q) taking values 32i + 8q .. +7 of row r for load i.  Row-major layout:
+// a load instruction covers 64 contiguous bytes of each of the 16 rows.  Blocked layout: the
+// same 16 x 256 values stored as one contiguous 8 KB block per (row block, step), so a load
+// instruction covers 1 KB.  Both read the same bytes; a word is written only if their xor
+// equals NEVER.
+template <bool BLOCKED>
+__global__ __launch_bounds__(256) void frag_read_kernel(const uint16_t* __restrict__ w, int rows, int K,
+                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int row0 = (blockIdx.x * 4 + wave) * 16;
+  if (row0 >= rows) return;
+  const int nsteps = K / 256;
+  auto at = [&](int st, int i) {
+    const size_t off = BLOCKED ? ((size_t)(row0 / 16) * nsteps + st) * 4096 + (size_t)i * 512 + lane * 8
+                               : (size_t)(row0 + r16) * K + (size_t)st * 256 + i * 32 + q * 8;
+    return *(const u32x4*)(w + off);
+  };
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 v0[8], v1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v0[i] = at(0, i);
+  for (int st = 0; st < nsteps; st += 2) {  // nsteps is even
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v1[i] = at(st + 1, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= v0[i];
+    if (st + 2 < nsteps) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v0[i] = at(st + 2, i);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= v1[i];
+  }
+  const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == NEVER) sink[blockIdx.x] = r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +132,21 @@ int moe_probe_copy(const void* src, void* dst, size_t n16, int grid, void* strea
 int moe_probe_mfma_bf16(int iters, int grid, void* sink, void* stream) {
   if (!sink || grid <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_bf16_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, (float*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// the few-token expert kernel's weight stream over a [rows, K] bf16 matrix, row-major
+// (blocked = 0) or in contiguous 16 x 256-value blocks (blocked = 1); rows a multiple of 64, K
+// of 512; one workgroup of 4 waves per 64 rows; sink: device, >= rows / 64 words
+int moe_probe_frag_read(const void* w, int rows, int K, int blocked, void* sink, void* stream) {
+  if (!w || !sink || rows <= 0 || rows % 64 || K <= 0 || K % 512) return -1;
+  const dim3 grid(rows / 64);
+  if (blocked)
+    hipLaunchKernelGGL(frag_read_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t*)w, rows, K,
+                       (uint32_t*)sink);
+  else
+    hipLaunchKernelGGL(frag_read_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t*)w, rows, K,
+                       (uint32_t*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
