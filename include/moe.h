@@ -56,7 +56,12 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed; moe_last_error() has the HIP text */
 } moe_status_t;
 
-typedef enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_MXFP4 = 1, MOE_WEIGHTS_MXFP8 = 2 } moe_weight_format_t;
+typedef enum {
+  MOE_WEIGHTS_BF16 = 0,
+  MOE_WEIGHTS_MXFP4 = 1,
+  MOE_WEIGHTS_MXFP8 = 2,
+  MOE_WEIGHTS_MXFP4_TILED = 3 /* MXFP4 in the kernels' tiled order (moe_pack_mxfp4) */
+} moe_weight_format_t;
 
 /* Activations of the routed experts' two matrix products.  MOE_ACT_BF16: x as given (bf16)
  * and h kept as two bf16 planes (about 16 significand bits).  MOE_ACT_MXFP8 (MXFP4 or MXFP8
@@ -95,6 +100,19 @@ typedef struct {
  *   MOE_WEIGHTS_MXFP8: gate [E,I,H], up [E,I,H], down [E,H,I] uint8 E4M3 codes (OCP FP8:
  *                      sign<<7 | exponent (bias 7)<<3 | mantissa; 0x7f/0xff NaN, never
  *                      given), scales as for MXFP4 (value = e4m3 * 2^(scale-127)).
+ *   MOE_WEIGHTS_MXFP4_TILED: the MXFP4 arrays (same values, same sizes) in the order the
+ *                      expert kernels read them, written by moe_pack_mxfp4; needs H and I
+ *                      multiples of 256.  Each matrix [N, Kd] (gate, up: N = I, Kd = H;
+ *                      down: N = H, Kd = I) is stored in blocks of 16 rows:
+ *                      codes: 1 KB per 16 rows x 128 values, block (b, s) at byte
+ *                        (b*(Kd/128) + s)*1024; in it, the 16 bytes at 16*(16*q + r) hold
+ *                        row 16b + r's values k = 128s + 32q .. +31 (two per byte, low
+ *                        nibble first), q = 0..3, r = 0..15;
+ *                      scales: 128 bytes per 16 rows x 256 values, block (b, t) at byte
+ *                        (b*(Kd/256) + t)*128; in it, byte 8*r + i is the scale of row
+ *                        16b + r's 32-value block 8t + i.
+ *                      A 16-lane x 4 load then reads 1 KB of contiguous codes per step (the
+ *                      row-major layout spreads it over 16 rows' half cache lines).
  *   Shared expert (bf16, required when S == 1, else ignored):
  *                      shared_gate [I,H], shared_up [I,H], shared_down [H,I]. */
 typedef struct {
@@ -206,6 +224,20 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
  * Enqueued on `stream`; rows = 0 is a no-op. */
 moe_status_t moe_quantise_mxfp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
                                 void* stream);
+
+/* MXFP4 weights from the row-major MOE_WEIGHTS_MXFP4 arrays into MOE_WEIGHTS_MXFP4_TILED
+ * order (the layout above), for `mats` consecutive matrices of N x Kd values each; weights
+ * are static, so this runs once when they are loaded (the hybrid-attention page, table
+ * 模型一览, gives the routed experts in MXFP4; their memory order is not fixed there).
+ *   codes      device uint8 [mats, N, Kd/2]   row-major E2M1 codes (16-byte aligned)
+ *   scales     device uint8 [mats, N, Kd/32]  row-major e8m0 scales (8-byte aligned)
+ *   codes_out  device uint8, mats * N * Kd/2 bytes (16-byte aligned; must not overlap codes)
+ *   scales_out device uint8, mats * N * Kd/32 bytes (8-byte aligned; must not overlap scales)
+ *   N          multiple of 16; Kd multiple of 256
+ * MOE_ERR_INVALID_ARG for a NULL pointer, bad sizes or overlapping buffers, MOE_ERR_ALIGNMENT
+ * for a misaligned pointer; mats = 0 is a no-op.  Enqueued on `stream`. */
+moe_status_t moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
+                            uint8_t* codes_out, uint8_t* scales_out, void* stream);
 
 /* Expert-bias update, the step after the layer in training (routing walk-through page,
  * section 三.3: every routed expert's selection bias is lowered when it is busy and raised

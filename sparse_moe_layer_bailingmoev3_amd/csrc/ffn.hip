@@ -74,6 +74,10 @@ struct FfnArgs {
   uint8_t* os;
   // the launch covers the tiles of experts e_lo .. e_hi-1 only (e_hi = 0: all E + S experts)
   int e_lo, e_hi;
+  // MXFP4 weights in the tiled order (codes in 1 KB blocks of 16 rows x 128 values, lane
+  // (r, q) holding row r's values 32q .. 32q+31 at byte 16 * (16q + r); scales in 128-byte
+  // blocks of 16 rows x 256 values, row r's eight block scales at byte 8r), else row-major
+  int tiled;
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -190,8 +194,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         constexpr int VPB = FP4 ? 2 : 1;  // values per byte
         const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / VPB);
         const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
-        wq[m][f] = base + row * (K / VPB) + k0 / VPB + q * (KS / 4 / VPB);
-        wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + q * (KS / 128);
+        if (FP4 && a.tiled) {  // (no split reduction for block-format weights: k0 = 0)
+          const size_t b16 = (size_t)(nbase + f * 16) / 16;
+          wq[m][f] = base + b16 * (K / 128) * 1024 + lane * 16;
+          wsc[m][f] = sbase + b16 * (K / 256) * 128 + r16 * 8 + q;
+        } else {
+          wq[m][f] = base + row * (K / VPB) + k0 / VPB + q * (KS / 4 / VPB);
+          wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + q * (KS / 128);
+        }
         wp[m][f] = nullptr;
       } else {
         const uint16_t* base = shared ? (const uint16_t*)(m == 0 ? a.sw0 : a.sw1)
@@ -242,10 +252,15 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
       for (int f = 0; f < RF; ++f) {
         if constexpr (MX) {
           constexpr int VPB = FP4 ? 2 : 1;
-          const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (KS / VPB);
+          // a row block is ROWS * K / VPB code bytes and ROWS * K / 32 scale bytes in both
+          // layouts; a 128-value step is 64 code bytes of a row (row-major) or a 1 KB block
+          // (tiled), 4 scale bytes of a row or half of a row's 8 bytes in a 128-byte block
+          const bool tl = FP4 && a.tiled;
+          const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (tl ? 1024 : KS / VPB);
 #pragma unroll
           for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + 16 * r);
-          st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) + (size_t)ks * (KS / 32)];
+          st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) +
+                                  (tl ? (size_t)(ks >> 1) * 128 + (ks & 1) * 4 : (size_t)ks * (KS / 32))];
         } else {
 #pragma unroll
           for (int s = 0; s < WREGS; ++s)
@@ -557,13 +572,16 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     wres[m] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, N * (K / VPB), 0x00020000);
     sres[m] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, N * (K / 32), 0x00020000);
   }
+  const bool tl = FP4 && a.tiled;
   int woff[RF], soff[RF];
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
-    const int row = nbase + f * 16 + r16;
-    woff[f] = row * (K / VPB) + q * 16;
-    soff[f] = row * (K / 32);
+    const int row = nbase + f * 16 + r16, b16 = (nbase + f * 16) / 16;
+    woff[f] = tl ? b16 * (K / 128) * 1024 + lane * 16 : row * (K / VPB) + q * 16;
+    soff[f] = tl ? b16 * (K / 256) * 128 + r16 * 8 : row * (K / 32);
   }
+  // per 128-value chunk: 64 code bytes of a row (row-major) or a 1 KB block (tiled)
+  const int wchunk = tl ? 1024 : 128 / VPB;
 
   // a weight stage holds the MFMA a operands themselves (an E2M1 operand's upper half stays
   // zero) and the rows' scale words of each chunk
@@ -600,8 +618,11 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     for (int k = 0; k < NSI; ++k) a8_dma4(ssrc[k] + i_ks * (KS / 32), st + sdst[k]);
   };
   auto issue_w = [&](WSt& w) {
-    const int wso = i_rb * ROWS * (K / VPB) + i_ks * (KS / VPB);
-    const int sso = i_rb * ROWS * (K / 32) + i_ks * (KS / 32);
+    // a row block is ROWS * K / VPB code bytes and ROWS * K / 32 scale bytes in both layouts;
+    // the step's scales are 4 * KC bytes of a row, at 8 bytes per row and 256 values (tiled)
+    const int wso = i_rb * ROWS * (K / VPB) + i_ks * KC * wchunk;
+    const int sso = i_rb * ROWS * (K / 32) + (tl ? (KC == 2 ? i_ks * 128 : (i_ks >> 1) * 128 + (i_ks & 1) * 4)
+                                                 : i_ks * (KS / 32));
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -609,7 +630,7 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           const u32x4 lo = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * (128 / VPB), wso, 0));
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * wchunk, wso, 0));
           w.w[m][f][c][0] = (int)lo[0];
           w.w[m][f][c][1] = (int)lo[1];
           w.w[m][f][c][2] = (int)lo[2];
@@ -807,6 +828,30 @@ __global__ __launch_bounds__(256) void mx8_quant_kernel(const uint16_t* __restri
 // costs ceil(n / 16) fragments rather than whole tiles (at 4096 tokens, 64-position tiles are
 // 65 % occupied by tokens, their 16-position fragments 90 %).  Bf16 activations take the
 // decoding kernel, MXFP8 activations the scaled MFMA.
+// row-major MXFP4 codes [mats, N, Kd/2] -> tiled order: 16-byte chunk i is lane l = 16q + r of
+// block (mb, s), mb = mat * N/16 + b, and takes row 16 mb + r's bytes 64s + 16q .. +15
+__global__ __launch_bounds__(256) void pack_mxfp4_codes_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                               int64_t n16, int Kd) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const int l = (int)(i & 63), ns = Kd / 128;
+  const int64_t blk = i >> 6, mb = blk / ns;
+  const int st = (int)(blk - mb * ns);
+  dst[i] = src[(mb * 16 + (l & 15)) * (Kd / 32) + st * 4 + (l >> 4)];
+}
+
+// row-major scales [mats, N, Kd/32] -> tiled order: 8-byte word i is row r = i mod 16 of block
+// (mb, t) and takes row 16 mb + r's scale bytes 8t .. 8t+7
+__global__ __launch_bounds__(256) void pack_mxfp4_scales_kernel(const uint64_t* __restrict__ src,
+                                                                uint64_t* __restrict__ dst, int64_t n8, int Kd) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int r = (int)(i & 15), nt = Kd / 256;
+  const int64_t blk = i >> 4, mb = blk / nt;
+  const int t = (int)(blk - mb * nt);
+  dst[i] = src[(mb * 16 + r) * nt + t];
+}
+
 template <int NW, int RF, int MF, int D, int MODE, int FMT, int KS, int ACT, bool PADDED>
 __device__ __forceinline__ void ffn_tile_mx(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                             int ksp, uint16_t* lds) {
@@ -1175,6 +1220,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   }
   gu.e_lo = dn.e_lo = 0;
   gu.e_hi = dn.e_hi = E;
+  gu.tiled = dn.tiled = w.tiled;
   const int64_t sh_tiles = S ? ((int64_t)T + p.bm - 1) / p.bm : 0;
   err = launch_mode<MODE_GATEUP>(p.mf_gate_up, gu, p.rbw_gate_up, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess) return err;
@@ -1197,6 +1243,18 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   dn_s.E = 1; dn_s.S = 0; dn_s.limit = shared_limit;
   dn_s.dense = 1; dn_s.out_bf16 = 0; dn_s.bm_list = 16 * sp.mf; dn_s.group_major = sp.group_major;
   return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_down_shared");
+}
+
+hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,
+                             uint8_t* codes_out, uint8_t* scales_out, hipStream_t s) {
+  if (mats < 0 || N <= 0 || N % 16 || Kd <= 0 || Kd % 256) return hipErrorInvalidValue;
+  const int64_t n16 = mats * N * (int64_t)(Kd / 32), n8 = mats * N * (int64_t)(Kd / 256);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_mxfp4_codes_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)codes, (u32x4*)codes_out, n16, Kd);
+  hipLaunchKernelGGL(pack_mxfp4_scales_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                     (const uint64_t*)scales, (uint64_t*)scales_out, n8, Kd);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales, hipStream_t s) {

@@ -79,6 +79,8 @@ def _bad(cfg_kw, T=64, code=None):
     (dict(num_shared_experts=2), -1),
     (dict(shared_intermediate_size=1024), -2),
     (dict(expert_weight_format=7), -1),
+    (dict(expert_weight_format=3, moe_intermediate_size=640), -2),   # tiled MXFP4: I % 256
+    (dict(expert_weight_format=3, hidden_size=2432), -2),            # tiled MXFP4: H % 256
     (dict(routed_scaling_factor=float("inf")), -1),
     (dict(swiglu_limit=float("nan")), -1),
 ])
@@ -169,3 +171,23 @@ def test_zero_tokens_is_a_no_op():
                            None, 0, None) == 0
     assert lib.moe_route(ctypes.byref(cfg), 0, None, None, None, None, None, None, 0, None) == 0
     assert lib.moe_combine(ctypes.byref(cfg), 0, None, None, None, None, None) == 0
+
+
+def test_pack_mxfp4_validation_on_the_host():
+    """moe_pack_mxfp4 checks sizes, pointers, alignment and overlap before it enqueues."""
+    lib = moe.load_library()
+    fake, M, N, Kd = 1 << 40, 4, 768, 2560
+    cb = M * N * Kd // 2
+    co, so = fake + (1 << 34), fake + (1 << 35)      # disjoint from the inputs
+    assert lib.moe_pack_mxfp4(fake, fake + (1 << 33), M, N, Kd, co, co + 16, None) == -1  # outputs overlap
+    assert b"overlap" in lib.moe_last_error()
+    assert lib.moe_pack_mxfp4(fake, fake + (1 << 33), M, N, Kd, fake + cb // 2, so, None) == -1
+    assert lib.moe_pack_mxfp4(fake, fake + (1 << 33), M, N, Kd, co, co + cb - 8, None) == -1
+    for n, k in ((760, 2560), (0, 2560), (768, 2432), (768, 0)):
+        assert lib.moe_pack_mxfp4(fake, fake + (1 << 33), M, n, k, co, so, None) == -1
+    assert lib.moe_pack_mxfp4(fake, fake + (1 << 33), -1, N, Kd, co, so, None) == -1
+    assert lib.moe_pack_mxfp4(None, fake + (1 << 33), M, N, Kd, co, so, None) == -1
+    assert lib.moe_pack_mxfp4(fake, None, M, N, Kd, co, so, None) == -1
+    assert lib.moe_pack_mxfp4(fake + 8, fake + (1 << 33), M, N, Kd, co, so, None) == -3   # codes not 16-aligned
+    assert lib.moe_pack_mxfp4(fake, fake + (1 << 33) + 4, M, N, Kd, co, so, None) == -3  # scales not 8-aligned
+    assert lib.moe_pack_mxfp4(None, None, 0, N, Kd, None, None, None) == 0             # nothing to pack
