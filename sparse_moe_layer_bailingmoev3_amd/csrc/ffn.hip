@@ -769,6 +769,12 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
   // that step g+D overwrites); issue step g+D's tokens; compute; issue step g+D's weights
   // into the slot compute(g) has just read; store a finished row block.  Every step issues
   // the same loads, so the count is exact; the loop is unrolled by D so slots are static.
+  // A down GEMM whose reduction is exactly NST steps (intermediate 768 at 256-value steps)
+  // keeps its whole h tile in the ring: the tokens are loaded during the first row block only
+  // and read again for the others, whose steps issue weight loads only (the wait then counts
+  // those) and need no barrier (LDS no longer changes).
+  const bool resident = D == 2 && MODE == MODE_DOWN && nsteps == NST;
+  constexpr int VM_WAIT_W = (D - 1) * NMAT * RF * (KC * WREGS + 1);
   const int padded_steps = (total_steps + D - 1) / D * D;
   int c_ks = 0, c_rb = 0;  // the compute side's k-step and row block
   for (int g0 = 0; g0 < padded_steps; g0 += D) {
@@ -776,10 +782,13 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     for (int j = 0; j < D; ++j) {
       const int g = g0 + j;
       const bool real = g < total_steps;
-      a8_wait_vmcnt<VM_WAIT>();
+      if (resident && g + 1 >= nsteps)
+        a8_wait_vmcnt<VM_WAIT_W>();  // step g+1 (the D-1 = 1 later step) loaded weights only
+      else
+        a8_wait_vmcnt<VM_WAIT>();
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      issue_t(g + D);
+      if (!resident || g < nsteps) __builtin_amdgcn_s_barrier();
+      if (!resident || g + D < nsteps) issue_t(g + D);
       if (real) compute(ws[j], g);
       issue_w(ws[j]);
       advance();

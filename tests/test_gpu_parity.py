@@ -361,6 +361,24 @@ def test_forward_tiny_act_mxfp8(wfmt, T, limit):
     check_forward(host_case(s, seed=24, T=T, experts=_tiny_block_experts(wfmt, 24)), tol=TOL_MXFP4)
 
 
+# the MXFP8-activation down GEMM keeps a tile's whole h in LDS when its reduction is three
+# steps: intermediate 384 (128-value steps) and 768 (256-value steps); several row blocks per
+# workgroup (hidden 512: four 128-row blocks) reuse it
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("I,T", [(384, 40), (384, 600), (768, 600), (768, 3000)])
+def test_forward_tiny_act_mxfp8_resident_h(wfmt, I, T):
+    base = CONFIGS["tiny"].with_(moe_intermediate_size=I, shared_intermediate_size=I)
+    s = base.with_(weight_format=wfmt, act_format="mxfp8")
+    quant = quantise_mxfp4 if wfmt == "mxfp4" else quantise_mxfp8
+    bf = gen_experts(base, seed=26)
+    ex = {}
+    for k in ("gate", "up", "down"):
+        qs = [quant(bf[k][e]) for e in range(s.E)]
+        ex[k + "_q"] = np.stack([a for a, _ in qs])
+        ex[k + "_s"] = np.stack([b for _, b in qs])
+    check_forward(host_case(s, seed=26, T=T, experts=ex), tol=TOL_MXFP4)
+
+
 def test_determinism_tiny_tiles():
     import torch
     c = host_case(CONFIGS["tiny"], seed=17, T=2048)
