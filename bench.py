@@ -116,14 +116,14 @@ def upload(shape, experts, seed=0):
     shared = [dev(sh[k], True) for k in ("gate", "up", "down")]
     if shape.weight_format in ("mxfp4", "mxfp8"):
         arrs = [dev(experts[k]) for k in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")]
-        if shape.weight_format == "mxfp4":
-            # MXFP4 experts in the kernels' tiled order, packed once on the device as at load time
-            E, I, H = shape.E, shape.I, shape.H
-            for j, (N, Kd) in enumerate(((I, H), (I, H), (H, I))):
-                qo, so = torch.empty_like(arrs[j]), torch.empty_like(arrs[3 + j])
-                moe.moe_pack_mxfp4(arrs[j], arrs[3 + j], E, N, Kd, qo, so)
-                arrs[j], arrs[3 + j] = qo, so
-            torch.cuda.synchronize()
+        # block-format experts in the kernels' tiled order, packed once on the device as at load
+        pack = moe.moe_pack_mxfp4 if shape.weight_format == "mxfp4" else moe.moe_pack_mxfp8
+        E, I, H = shape.E, shape.I, shape.H
+        for j, (N, Kd) in enumerate(((I, H), (I, H), (H, I))):
+            qo, so = torch.empty_like(arrs[j]), torch.empty_like(arrs[3 + j])
+            pack(arrs[j], arrs[3 + j], E, N, Kd, qo, so)
+            arrs[j], arrs[3 + j] = qo, so
+        torch.cuda.synchronize()
         w = moe.MoEExpertWeights(*arrs, *shared)
     else:
         w = moe.MoEExpertWeights(*[dev(experts[k], True) for k in ("gate", "up", "down")],
@@ -140,7 +140,7 @@ def cfg_for(shape):
                          norm_topk_prob=int(shape.norm_topk_prob), routed_scaling_factor=shape.routed_scaling_factor,
                          swiglu_limit=shape.swiglu_limit, shared_swiglu_limit=shape.shared_swiglu_limit,
                          expert_weight_format={"bf16": moe.MOE_WEIGHTS_BF16, "mxfp4": moe.MOE_WEIGHTS_MXFP4_TILED,
-                                               "mxfp8": moe.MOE_WEIGHTS_MXFP8}[shape.weight_format],
+                                               "mxfp8": moe.MOE_WEIGHTS_MXFP8_TILED}[shape.weight_format],
                          expert_act_format=moe.MOE_ACT_MXFP8 if shape.act_format == "mxfp8" else moe.MOE_ACT_BF16)
 
 
@@ -824,7 +824,7 @@ def main():
                    "T": shape.T, "hidden_size": shape.H, "num_experts": shape.E, "moe_intermediate_size": shape.I,
                    "n_group": shape.G, "topk_group": shape.TG, "num_experts_per_tok": shape.K,
                    "weights": shape.weight_format + (" (tiled order, packed once at load)"
-                                                     if shape.weight_format == "mxfp4" else ""),
+                                                     if shape.weight_format != "bf16" else ""),
                    "parallelism": "single GPU"},
         "roofline": roofline(shape, r, measured=measured),
         "layer": layer_summary(shape, r, measured),
@@ -873,8 +873,9 @@ def main():
             log(f"measuring {name} T={p.T}")
             rp = measure(p, dp, max(5, args.steps // 3), 3, hip)
             desc = {"skewed": ", clamp 4 / 7, clustered tokens, bias N(0,0.5)", "mxfp4": ", routed experts MXFP4 (tiled order)",
-                    "mxfp8": ", routed experts MXFP8", "mxfp4_a8": ", routed experts MXFP4 (tiled order), MXFP8 activations",
-                    "mxfp8_a8": ", routed experts MXFP8, MXFP8 activations"}.get(name, "")
+                    "mxfp8": ", routed experts MXFP8 (tiled order)",
+                    "mxfp4_a8": ", routed experts MXFP4 (tiled order), MXFP8 activations",
+                    "mxfp8_a8": ", routed experts MXFP8 (tiled order), MXFP8 activations"}.get(name, "")
             line["secondary"][name] = {
                 "workload": f"{name}: T={p.T}, same layer{desc}",
                 "value": round(p.T / (rp["wall_ms"] * 1e-3), 1), "unit": "tokens/s",

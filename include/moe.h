@@ -60,7 +60,8 @@ typedef enum {
   MOE_WEIGHTS_BF16 = 0,
   MOE_WEIGHTS_MXFP4 = 1,
   MOE_WEIGHTS_MXFP8 = 2,
-  MOE_WEIGHTS_MXFP4_TILED = 3 /* MXFP4 in the kernels' tiled order (moe_pack_mxfp4) */
+  MOE_WEIGHTS_MXFP4_TILED = 3, /* MXFP4 in the kernels' tiled order (moe_pack_mxfp4) */
+  MOE_WEIGHTS_MXFP8_TILED = 4  /* MXFP8 in the kernels' tiled order (moe_pack_mxfp8) */
 } moe_weight_format_t;
 
 /* Activations of the routed experts' two matrix products.  MOE_ACT_BF16: x as given (bf16)
@@ -113,6 +114,11 @@ typedef struct {
  *                        16b + r's 32-value block 8t + i.
  *                      A 16-lane x 4 load then reads 1 KB of contiguous codes per step (the
  *                      row-major layout spreads it over 16 rows' half cache lines).
+ *   MOE_WEIGHTS_MXFP8_TILED: the MXFP8 arrays in the same manner (moe_pack_mxfp8; H and I
+ *                      multiples of 256): codes 2 KB per 16 rows x 128 values, block (b, s) at
+ *                      byte (b*(Kd/128) + s)*2048; in it, the 16 bytes at 1024*p + 16*(16*q + r)
+ *                      hold row 16b + r's values k = 128s + 64p + 16q .. +15 (p = 0, 1: the
+ *                      scaled MFMA's E4M3 operand halves); scales as for MOE_WEIGHTS_MXFP4_TILED.
  *   Shared expert (bf16, required when S == 1, else ignored):
  *                      shared_gate [I,H], shared_up [I,H], shared_down [H,I]. */
 typedef struct {
@@ -237,6 +243,12 @@ moe_status_t moe_quantise_mxfp8(const void* x, int64_t rows, int32_t cols, uint8
  * MOE_ERR_INVALID_ARG for a NULL pointer, bad sizes or overlapping buffers, MOE_ERR_ALIGNMENT
  * for a misaligned pointer; mats = 0 is a no-op.  Enqueued on `stream`. */
 moe_status_t moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
+                            uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
+/* The same for MXFP8 weights (MOE_WEIGHTS_MXFP8 -> MOE_WEIGHTS_MXFP8_TILED): codes [mats, N, Kd]
+ * (one E4M3 code per byte) and scales [mats, N, Kd/32], outputs of the same sizes; the same
+ * requirements and errors as moe_pack_mxfp4. */
+moe_status_t moe_pack_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
                             uint8_t* codes_out, uint8_t* scales_out, void* stream);
 
 /* Expert-bias update, the step after the layer in training (routing walk-through page,

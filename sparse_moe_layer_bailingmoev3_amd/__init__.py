@@ -18,8 +18,9 @@ from typing import Optional
 __all__ = ["MoEConfig", "MoEExpertWeights", "MoEError", "lib_path", "load_library", "moe_workspace_size",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
            "moe_forward_timed", "moe_update_expert_bias", "moe_dense_ffn_workspace_size", "moe_dense_ffn",
-           "moe_forward_noalloc", "moe_quantise_mxfp8", "moe_pack_mxfp4", "moe_status_string",
+           "moe_forward_noalloc", "moe_quantise_mxfp8", "moe_pack_mxfp4", "moe_pack_mxfp8", "moe_status_string",
            "MOE_WEIGHTS_BF16", "MOE_WEIGHTS_MXFP4", "MOE_WEIGHTS_MXFP8", "MOE_WEIGHTS_MXFP4_TILED",
+           "MOE_WEIGHTS_MXFP8_TILED",
            "MOE_ACT_BF16", "MOE_ACT_MXFP8",
            "EXPORTED_SYMBOLS"]
 
@@ -27,13 +28,14 @@ MOE_WEIGHTS_BF16 = 0
 MOE_WEIGHTS_MXFP4 = 1
 MOE_WEIGHTS_MXFP8 = 2
 MOE_WEIGHTS_MXFP4_TILED = 3
+MOE_WEIGHTS_MXFP8_TILED = 4
 MOE_ACT_BF16 = 0
 MOE_ACT_MXFP8 = 1
 
 EXPORTED_SYMBOLS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_forward", "moe_forward_traced", "moe_forward_timed", "moe_update_expert_bias",
                     "moe_dense_ffn_workspace_size", "moe_dense_ffn", "moe_forward_noalloc", "moe_quantise_mxfp8",
-                    "moe_pack_mxfp4", "moe_status_string", "moe_last_error")
+                    "moe_pack_mxfp4", "moe_pack_mxfp8", "moe_status_string", "moe_last_error")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -103,6 +105,7 @@ def load_library():
         "moe_forward_noalloc": [C, I64, P, P, P, W, P, P, P, P, P],
         "moe_quantise_mxfp8": [P, I64, ctypes.c_int32, P, P, P],
         "moe_pack_mxfp4": [P, P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P],
+        "moe_pack_mxfp8": [P, P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -241,6 +244,13 @@ def moe_pack_mxfp4(codes, scales, mats, N, Kd, codes_out, scales_out, stream=Non
     """Row-major MXFP4 codes [mats, N, Kd/2] and scales [mats, N, Kd/32] -> the tiled order of
     MOE_WEIGHTS_MXFP4_TILED (same sizes)."""
     _check(load_library().moe_pack_mxfp4(_ptr(codes), _ptr(scales), mats, N, Kd, _ptr(codes_out), _ptr(scales_out),
+                                         _stream(stream)))
+
+
+def moe_pack_mxfp8(codes, scales, mats, N, Kd, codes_out, scales_out, stream=None):
+    """Row-major MXFP8 codes [mats, N, Kd] and scales [mats, N, Kd/32] -> the tiled order of
+    MOE_WEIGHTS_MXFP8_TILED (same sizes)."""
+    _check(load_library().moe_pack_mxfp8(_ptr(codes), _ptr(scales), mats, N, Kd, _ptr(codes_out), _ptr(scales_out),
                                          _stream(stream)))
 
 

@@ -178,9 +178,12 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
   }
 
   // weight rows of this lane.  bf16: sub-step s of a step reads k = 32s + 8q .. +7, so
-  // one load instruction covers 64 contiguous bytes of each of the 16 rows.  MXFP4 / MXFP8:
-  // lane group q owns the 32-value block q of the step (16 / 32 bytes of codes, one scale
-  // byte) and sub-step s uses its codes 8s .. 8s+7.
+  // one load instruction covers 64 contiguous bytes of each of the 16 rows.  MXFP4: lane
+  // group q owns the 32-value block q of the step (16 bytes of codes, one scale byte) and
+  // sub-step s uses its codes 8s .. 8s+7.  MXFP8: lane group q owns values 16q .. 16q+15 and
+  // 64+16q .. 64+16q+15 of the step (the scaled MFMA's E4M3 operand layout, so that one tiled
+  // order serves both kernels), sub-step s values 16q + 8(s&1) + 64(s>>1) .. +7, whose block
+  // scale is byte (q>>1) + 2(s>>1) of the row's scale word of the step.
   const int nbase = rb0 * ROWS + wave * RF * 16;
   const uint16_t* wp[NMAT][RF];
   const uint8_t* wq[NMAT][RF];
@@ -194,13 +197,13 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         constexpr int VPB = FP4 ? 2 : 1;  // values per byte
         const uint8_t* base = (const uint8_t*)(m == 0 ? a.w0 : a.w1) + (size_t)e * N * (K / VPB);
         const uint8_t* sbase = (m == 0 ? a.s0 : a.s1) + (size_t)e * N * (K / 32);
-        if (FP4 && a.tiled) {  // (no split reduction for block-format weights: k0 = 0)
+        if (a.tiled) {  // (no split reduction for block-format weights: k0 = 0)
           const size_t b16 = (size_t)(nbase + f * 16) / 16;
-          wq[m][f] = base + b16 * (K / 128) * 1024 + lane * 16;
-          wsc[m][f] = sbase + b16 * (K / 256) * 128 + r16 * 8 + q;
+          wq[m][f] = base + b16 * (K / 128) * 1024 * WREGS + lane * 16;
+          wsc[m][f] = sbase + b16 * (K / 256) * 128 + r16 * 8 + (FP4 ? q : 0);
         } else {
-          wq[m][f] = base + row * (K / VPB) + k0 / VPB + q * (KS / 4 / VPB);
-          wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + q * (KS / 128);
+          wq[m][f] = base + row * (K / VPB) + k0 / VPB + q * 16;
+          wsc[m][f] = sbase + row * (K / 32) + k0 / 32 + (FP4 ? q : 0);
         }
         wp[m][f] = nullptr;
       } else {
@@ -253,14 +256,19 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         if constexpr (MX) {
           constexpr int VPB = FP4 ? 2 : 1;
           // a row block is ROWS * K / VPB code bytes and ROWS * K / 32 scale bytes in both
-          // layouts; a 128-value step is 64 code bytes of a row (row-major) or a 1 KB block
-          // (tiled), 4 scale bytes of a row or half of a row's 8 bytes in a 128-byte block
-          const bool tl = FP4 && a.tiled;
-          const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (tl ? 1024 : KS / VPB);
+          // layouts; a 128-value step is 128 / VPB code bytes of a row (row-major) or a block
+          // of 1 KB per load (tiled), 4 scale bytes of a row or half of a row's 8 bytes in a
+          // 128-byte block.  MXFP8 takes the row's whole scale word, MXFP4 the lane's byte.
+          const bool tl = a.tiled;
+          const uint8_t* src = wq[m][f] + (size_t)rbi * ROWS * (K / VPB) + (size_t)ks * (tl ? 1024 * WREGS : KS / VPB);
 #pragma unroll
-          for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + 16 * r);
-          st.sc[m][f] = wsc[m][f][(size_t)rbi * ROWS * (K / 32) +
-                                  (tl ? (size_t)(ks >> 1) * 128 + (ks & 1) * 4 : (size_t)ks * (KS / 32))];
+          for (int r = 0; r < WREGS; ++r) st.w[m][f][r] = *(const u32x4*)(src + (tl ? 1024 : 64) * r);
+          const size_t so = (size_t)rbi * ROWS * (K / 32) +
+                            (tl ? (size_t)(ks >> 1) * 128 + (ks & 1) * 4 : (size_t)ks * (KS / 32));
+          if constexpr (FP4)
+            st.sc[m][f] = wsc[m][f][so];
+          else
+            st.sc[m][f] = *(const uint32_t*)(wsc[m][f] + so);
         } else {
 #pragma unroll
           for (int s = 0; s < WREGS; ++s)
@@ -268,20 +276,27 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         }
       }
   };
-  // the 8 weights of sub-step s (codes 8s .. 8s+7 of the lane's 32-value block) as bf16
+  // the 8 weights of sub-step s as bf16 (MXFP4: codes 8s .. 8s+7 of the lane's block; MXFP8:
+  // bytes 8(s&1) .. +7 of its load s>>1)
   auto decode_mx = [&](const WStage<NMAT, RF, WREGS>& st, int m, int f, int s) -> u32x4 {
-    const float sc = e8m0_to_f32(st.sc[m][f]);
     if constexpr (FP4) {
-      return fp4x8_to_bf16x8(st.w[m][f][0][s], sc);
+      return fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
     } else {
+      const float sc = e8m0_to_f32((st.sc[m][f] >> (8 * ((q >> 1) + 2 * (s >> 1)))) & 0xFFu);
       return fp8x8_to_bf16x8(st.w[m][f][s >> 1][(2 * s) & 3], st.w[m][f][s >> 1][(2 * s + 1) & 3], sc);
     }
+  };
+  // the k offset, within a step, of the lane's sub-step s values (both operands)
+  auto kcol = [&](int s) {
+    if constexpr (!MX) return s * 32 + q * 8;
+    else if constexpr (FP4) return q * 32 + s * 8;
+    else return q * 16 + (s & 1) * 8 + (s >> 1) * 64;
   };
   auto compute_at_use = [&](const WStage<NMAT, RF, WREGS>& st, int buf) {
     const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      const int col = MX ? q * 32 + s * 8 : s * 32 + q * 8;
+      const int col = kcol(s);
       u32x4 wf[NMAT][RF];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
@@ -318,7 +333,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
     const uint16_t* L = lds + buf * NTP * BM * LROW + r16 * LROW;
     u32x4 tf[2][NTP][MF];
     auto read_frags = [&](u32x4 (&t)[NTP][MF], int s) {
-      const int col = MX ? q * 32 + s * 8 : s * 32 + q * 8;
+      const int col = kcol(s);
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -572,16 +587,17 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
     wres[m] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, N * (K / VPB), 0x00020000);
     sres[m] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, N * (K / 32), 0x00020000);
   }
-  const bool tl = FP4 && a.tiled;
+  const bool tl = a.tiled;
   int woff[RF], soff[RF];
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
     const int row = nbase + f * 16 + r16, b16 = (nbase + f * 16) / 16;
-    woff[f] = tl ? b16 * (K / 128) * 1024 + lane * 16 : row * (K / VPB) + q * 16;
+    woff[f] = tl ? b16 * (K / 128) * 1024 * WREGS + lane * 16 : row * (K / VPB) + q * 16;
     soff[f] = tl ? b16 * (K / 256) * 128 + r16 * 8 : row * (K / 32);
   }
-  // per 128-value chunk: 64 code bytes of a row (row-major) or a 1 KB block (tiled)
-  const int wchunk = tl ? 1024 : 128 / VPB;
+  // per 128-value chunk: 128 / VPB code bytes of a row (row-major) or 1 KB per load (tiled);
+  // an E4M3 operand's second 16 bytes 64 bytes on in the row or one 1 KB load on
+  const int wchunk = tl ? 1024 * WREGS : 128 / VPB, whi = tl ? 1024 : 64;
 
   // a weight stage holds the MFMA a operands themselves (an E2M1 operand's upper half stays
   // zero) and the rows' scale words of each chunk
@@ -637,7 +653,7 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
           w.w[m][f][c][3] = (int)lo[3];
           if constexpr (!FP4) {
             const u32x4 hi = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * 128 + 64, wso, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[m], woff[f] + c * wchunk + whi, wso, 0));
             w.w[m][f][c][4] = (int)hi[0];
             w.w[m][f][c][5] = (int)hi[1];
             w.w[m][f][c][6] = (int)hi[2];
@@ -847,6 +863,18 @@ __global__ __launch_bounds__(256) void pack_mxfp4_codes_kernel(const u32x4* __re
   const int64_t blk = i >> 6, mb = blk / ns;
   const int st = (int)(blk - mb * ns);
   dst[i] = src[(mb * 16 + (l & 15)) * (Kd / 32) + st * 4 + (l >> 4)];
+}
+
+// row-major MXFP8 codes [mats, N, Kd] -> tiled order: 16-byte chunk i is lane l = 16q + r of
+// half p of block (mb, s) and takes row 16 mb + r's bytes 128s + 64p + 16q .. +15
+__global__ __launch_bounds__(256) void pack_mxfp8_codes_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                               int64_t n16, int Kd) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const int l = (int)(i & 63), half = (int)((i >> 6) & 1), ns = Kd / 128;
+  const int64_t blk = i >> 7, mb = blk / ns;
+  const int st = (int)(blk - mb * ns);
+  dst[i] = src[(mb * 16 + (l & 15)) * (Kd / 16) + st * 8 + half * 4 + (l >> 4)];
 }
 
 // row-major scales [mats, N, Kd/32] -> tiled order: 8-byte word i is row r = i mod 16 of block
@@ -1268,13 +1296,19 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_down_shared");
 }
 
-hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,
-                             uint8_t* codes_out, uint8_t* scales_out, hipStream_t s) {
-  if (mats < 0 || N <= 0 || N % 16 || Kd <= 0 || Kd % 256) return hipErrorInvalidValue;
-  const int64_t n16 = mats * N * (int64_t)(Kd / 32), n8 = mats * N * (int64_t)(Kd / 256);
+hipError_t launch_pack_mx(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,
+                          uint8_t* codes_out, uint8_t* scales_out, hipStream_t s) {
+  if ((fmt != FMT_MXFP4 && fmt != FMT_MXFP8) || mats < 0 || N <= 0 || N % 16 || Kd <= 0 || Kd % 256)
+    return hipErrorInvalidValue;
+  const int vpb = fmt == FMT_MXFP4 ? 2 : 1;
+  const int64_t n16 = mats * N * (int64_t)(Kd / vpb / 16), n8 = mats * N * (int64_t)(Kd / 256);
   if (n16 == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_mxfp4_codes_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
-                     (const u32x4*)codes, (u32x4*)codes_out, n16, Kd);
+  if (fmt == FMT_MXFP4)
+    hipLaunchKernelGGL(pack_mxfp4_codes_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       (const u32x4*)codes, (u32x4*)codes_out, n16, Kd);
+  else
+    hipLaunchKernelGGL(pack_mxfp8_codes_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       (const u32x4*)codes, (u32x4*)codes_out, n16, Kd);
   hipLaunchKernelGGL(pack_mxfp4_scales_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
                      (const uint64_t*)scales, (uint64_t*)scales_out, n8, Kd);
   return hipGetLastError();

@@ -79,11 +79,14 @@ moe_status_t validate_config(const moe_config_t* c, int64_t T) {
     return fail(MOE_ERR_UNSUPPORTED, "shared_intermediate_size %d must equal moe_intermediate_size %d",
                 c->shared_intermediate_size, c->moe_intermediate_size);
   if (c->expert_weight_format != MOE_WEIGHTS_BF16 && c->expert_weight_format != MOE_WEIGHTS_MXFP4 &&
-      c->expert_weight_format != MOE_WEIGHTS_MXFP8 && c->expert_weight_format != MOE_WEIGHTS_MXFP4_TILED)
+      c->expert_weight_format != MOE_WEIGHTS_MXFP8 && c->expert_weight_format != MOE_WEIGHTS_MXFP4_TILED &&
+      c->expert_weight_format != MOE_WEIGHTS_MXFP8_TILED)
     return fail(MOE_ERR_INVALID_ARG, "expert_weight_format %d is unknown", c->expert_weight_format);
-  if (c->expert_weight_format == MOE_WEIGHTS_MXFP4_TILED && (c->hidden_size % 256 || c->moe_intermediate_size % 256))
-    return fail(MOE_ERR_UNSUPPORTED, "tiled MXFP4 weights need hidden_size (%d) and moe_intermediate_size (%d) "
-                "multiples of 256", c->hidden_size, c->moe_intermediate_size);
+  const bool tiled = c->expert_weight_format == MOE_WEIGHTS_MXFP4_TILED ||
+                     c->expert_weight_format == MOE_WEIGHTS_MXFP8_TILED;
+  if (tiled && (c->hidden_size % 256 || c->moe_intermediate_size % 256))
+    return fail(MOE_ERR_UNSUPPORTED, "tiled block-format weights need hidden_size (%d) and moe_intermediate_size "
+                "(%d) multiples of 256", c->hidden_size, c->moe_intermediate_size);
   if (c->expert_act_format != MOE_ACT_BF16 && c->expert_act_format != MOE_ACT_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "expert_act_format %d is unknown", c->expert_act_format);
   if (c->expert_act_format == MOE_ACT_MXFP8 && c->expert_weight_format == MOE_WEIGHTS_BF16)
@@ -98,13 +101,13 @@ moe_status_t validate_config(const moe_config_t* c, int64_t T) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// the kernels' weight-format code (the two MXFP4 orders share the kernels; the tiled one sets
-// FfnWeights::tiled)
+// the kernels' weight-format code (the row-major and tiled orders of a format share the
+// kernels; the tiled one sets FfnWeights::tiled)
 int wfmt(const moe_config_t* c) {
-  return c->expert_weight_format == MOE_WEIGHTS_MXFP4 || c->expert_weight_format == MOE_WEIGHTS_MXFP4_TILED
-             ? moe::FMT_MXFP4
-         : c->expert_weight_format == MOE_WEIGHTS_MXFP8 ? moe::FMT_MXFP8
-                                                         : moe::FMT_BF16;
+  const int f = c->expert_weight_format;
+  return f == MOE_WEIGHTS_MXFP4 || f == MOE_WEIGHTS_MXFP4_TILED   ? moe::FMT_MXFP4
+         : f == MOE_WEIGHTS_MXFP8 || f == MOE_WEIGHTS_MXFP8_TILED ? moe::FMT_MXFP8
+                                                                    : moe::FMT_BF16;
 }
 
 struct Layout {
@@ -168,6 +171,9 @@ moe_status_t check_weights(const moe_config_t* c, const moe_expert_weights_t* w)
   if (c->expert_weight_format != MOE_WEIGHTS_BF16) {
     if (!w->gate_scale || !w->up_scale || !w->down_scale)
       return fail(MOE_ERR_INVALID_ARG, "MXFP4 and MXFP8 weights need gate_scale, up_scale and down_scale");
+    MOE_CHECK_PTR(w->gate_scale, "weights->gate_scale");
+    MOE_CHECK_PTR(w->up_scale, "weights->up_scale");
+    MOE_CHECK_PTR(w->down_scale, "weights->down_scale");
   }
   if (c->num_shared_experts) {
     MOE_CHECK_PTR(w->shared_gate, "weights->shared_gate");
@@ -183,7 +189,7 @@ moe::FfnWeights ffn_weights(const moe_config_t* c, const moe_expert_weights_t* w
   f.gate_scale = w->gate_scale; f.up_scale = w->up_scale; f.down_scale = w->down_scale;
   f.sh_gate = w->shared_gate; f.sh_up = w->shared_up; f.sh_down = w->shared_down;
   f.fmt = wfmt(c);
-  f.tiled = c->expert_weight_format == MOE_WEIGHTS_MXFP4_TILED;
+  f.tiled = c->expert_weight_format == MOE_WEIGHTS_MXFP4_TILED || c->expert_weight_format == MOE_WEIGHTS_MXFP8_TILED;
   return f;
 }
 
@@ -464,8 +470,8 @@ moe_status_t moe_quantise_mxfp8(const void* x, int64_t rows, int32_t cols, uint8
   return MOE_OK;
 }
 
-moe_status_t moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
-                            uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+static moe_status_t pack_mx(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N,
+                            int32_t Kd, uint8_t* codes_out, uint8_t* scales_out, void* stream) {
   g_last_error.clear();
   if (mats < 0) return fail(MOE_ERR_INVALID_ARG, "mats = %lld must be >= 0", (long long)mats);
   if (N <= 0 || N % 16) return fail(MOE_ERR_INVALID_ARG, "N = %d must be a positive multiple of 16", N);
@@ -476,16 +482,27 @@ moe_status_t moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t
   if (!scales || !scales_out) return fail(MOE_ERR_INVALID_ARG, "scales and scales_out must not be NULL");
   if (((uintptr_t)scales & 7u) || ((uintptr_t)scales_out & 7u))
     return fail(MOE_ERR_ALIGNMENT, "scales and scales_out must be 8-byte aligned");
-  const uintptr_t cb = (uintptr_t)mats * (uintptr_t)N * (uintptr_t)(Kd / 2), sb = cb / 16;
+  const uintptr_t cb = (uintptr_t)mats * (uintptr_t)N * (uintptr_t)(fmt == moe::FMT_MXFP4 ? Kd / 2 : Kd);
+  const uintptr_t sb = (uintptr_t)mats * (uintptr_t)N * (uintptr_t)(Kd / 32);
   auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
     return (uintptr_t)a < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)a + na;
   };
   if (overlap(codes_out, cb, codes, cb) || overlap(codes_out, cb, scales, sb) || overlap(codes_out, cb, scales_out, sb) ||
       overlap(scales_out, sb, codes, cb) || overlap(scales_out, sb, scales, sb))
     return fail(MOE_ERR_INVALID_ARG, "the output arrays must not overlap each other or the inputs");
-  hipError_t e = moe::launch_pack_mxfp4(codes, scales, mats, N, Kd, codes_out, scales_out, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "MXFP4 pack launch");
+  hipError_t e = moe::launch_pack_mx(fmt, codes, scales, mats, N, Kd, codes_out, scales_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block-format pack launch");
   return MOE_OK;
+}
+
+moe_status_t moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
+                            uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+  return pack_mx(moe::FMT_MXFP4, codes, scales, mats, N, Kd, codes_out, scales_out, stream);
+}
+
+moe_status_t moe_pack_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t mats, int32_t N, int32_t Kd,
+                            uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+  return pack_mx(moe::FMT_MXFP8, codes, scales, mats, N, Kd, codes_out, scales_out, stream);
 }
 
 moe_status_t moe_update_expert_bias(const moe_config_t* cfg, const int32_t* expert_counts, float* expert_bias,

@@ -111,7 +111,7 @@ struct FfnWeights {
   const uint8_t* gate_scale; const uint8_t* up_scale; const uint8_t* down_scale;
   const void* sh_gate; const void* sh_up; const void* sh_down;
   int fmt;
-  int tiled;  // MXFP4 in the tiled order (moe_pack_mxfp4)
+  int tiled;  // MXFP4 / MXFP8 in the tiled order (moe_pack_mxfp4 / moe_pack_mxfp8)
 };
 struct FfnPlan {
   int mf;      // 16-token fragments per tile of the tile list (1, 2, 4, 8; 16 for bf16 weights)
@@ -148,9 +148,10 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr, const ActBufs* ab = nullptr);
 // bf16 [rows, cols] -> MXFP8 codes [rows, cols] and e8m0 scales [rows, cols/32] (cols % 32 == 0)
-// row-major MXFP4 arrays of `mats` matrices [N, Kd] -> the tiled order of moe_pack_mxfp4
-hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,
-                             uint8_t* codes_out, uint8_t* scales_out, hipStream_t s);
+// row-major MXFP4 (fmt FMT_MXFP4) or MXFP8 arrays of `mats` matrices [N, Kd] -> the tiled order
+// of moe_pack_mxfp4 / moe_pack_mxfp8
+hipError_t launch_pack_mx(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,
+                          uint8_t* codes_out, uint8_t* scales_out, hipStream_t s);
 hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,
                             hipStream_t s);
 

@@ -81,6 +81,7 @@ def _bad(cfg_kw, T=64, code=None):
     (dict(expert_weight_format=7), -1),
     (dict(expert_weight_format=3, moe_intermediate_size=640), -2),   # tiled MXFP4: I % 256
     (dict(expert_weight_format=3, hidden_size=2432), -2),            # tiled MXFP4: H % 256
+    (dict(expert_weight_format=4, moe_intermediate_size=640), -2),   # tiled MXFP8: I % 256
     (dict(routed_scaling_factor=float("inf")), -1),
     (dict(swiglu_limit=float("nan")), -1),
 ])
@@ -191,3 +192,6 @@ def test_pack_mxfp4_validation_on_the_host():
     assert lib.moe_pack_mxfp4(fake + 8, fake + (1 << 33), M, N, Kd, co, so, None) == -3   # codes not 16-aligned
     assert lib.moe_pack_mxfp4(fake, fake + (1 << 33) + 4, M, N, Kd, co, so, None) == -3  # scales not 8-aligned
     assert lib.moe_pack_mxfp4(None, None, 0, N, Kd, None, None, None) == 0             # nothing to pack
+    # MXFP8: codes are Kd bytes per row, so an output one MXFP4 size away still overlaps
+    assert lib.moe_pack_mxfp8(fake, fake + (1 << 33), M, N, Kd, fake + cb, so, None) == -1
+    assert lib.moe_pack_mxfp8(fake, fake + (1 << 33), M, N, 2432, co, so, None) == -1

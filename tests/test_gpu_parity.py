@@ -244,22 +244,24 @@ def test_forward_tiny_mxfp8(T, limit):
 
 
 def _tiled_case(dev):
-    """A copy of a device case whose MXFP4 experts are packed on the GPU into the tiled order
-    (moe_pack_mxfp4) and named so in the config."""
+    """A copy of a device case whose MXFP4 or MXFP8 experts are packed on the GPU into the
+    tiled order (moe_pack_mxfp4 / moe_pack_mxfp8) and named so in the config."""
     import copy
     import torch
     import sparse_moe_layer_bailingmoev3_amd as moe
     s = dev.c.shape
+    fp4 = s.weight_format == "mxfp4"
+    pack = moe.moe_pack_mxfp4 if fp4 else moe.moe_pack_mxfp8
     keep = dev.weights._keep
     packed = []
     for q, sc, (N, Kd) in zip(keep[0:3], keep[3:6], ((s.I, s.H), (s.I, s.H), (s.H, s.I))):
         qo, so = torch.empty_like(q), torch.empty_like(sc)
-        moe.moe_pack_mxfp4(q, sc, s.E, N, Kd, qo, so)
+        pack(q, sc, s.E, N, Kd, qo, so)
         packed.append((qo, so))
     torch.cuda.synchronize()
     t = copy.copy(dev)
     t.cfg = type(dev.cfg).from_buffer_copy(dev.cfg)
-    t.cfg.expert_weight_format = moe.MOE_WEIGHTS_MXFP4_TILED
+    t.cfg.expert_weight_format = moe.MOE_WEIGHTS_MXFP4_TILED if fp4 else moe.MOE_WEIGHTS_MXFP8_TILED
     t.weights = moe.MoEExpertWeights(*[p[0] for p in packed], *[p[1] for p in packed], *keep[6:9])
     return t
 
@@ -294,27 +296,50 @@ def test_pack_mxfp4_layout():
         np.testing.assert_array_equal(so.cpu().numpy(), want_s)
 
 
-# Tiled MXFP4 weights give the row-major layer bit for bit (the same products in the same
-# order), with bf16 and MXFP8 activations, 16-, 64- and 128-token tiles; intermediate 256 (the
-# tiled order needs multiples of 256); and the tiled layer against the oracle once
+def test_pack_mxfp8_layout():
+    """moe_pack_mxfp8 against moe.h's tiled MXFP8 order, written out with numpy reshapes: 2 KB
+    blocks (b, s) whose 16 bytes at 1024p + 16*(16q + r) are row 16b + r's bytes
+    128s + 64p + 16q .. +15; scales as for MXFP4."""
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    rng = np.random.default_rng(32)
+    for M, N, Kd in ((3, 48, 512), (2, 2560, 768)):
+        say(f"[gpu] moe_pack_mxfp8 {M}x{N}x{Kd}")
+        q = rng.integers(0, 256, size=(M, N, Kd), dtype=np.uint8)
+        sc = rng.integers(0, 256, size=(M, N, Kd // 32), dtype=np.uint8)
+        qo = torch.empty(q.size, dtype=torch.uint8, device="cuda")
+        so = torch.empty(sc.size, dtype=torch.uint8, device="cuda")
+        moe.moe_pack_mxfp8(to_dev(q), to_dev(sc), M, N, Kd, qo, so)
+        torch.cuda.synchronize()
+        want_q = q.reshape(M, N // 16, 16, Kd // 128, 2, 4, 16).transpose(0, 1, 3, 4, 5, 2, 6).ravel()
+        want_s = sc.reshape(M, N // 16, 16, Kd // 256, 8).transpose(0, 1, 3, 2, 4).ravel()
+        np.testing.assert_array_equal(qo.cpu().numpy(), want_q)
+        np.testing.assert_array_equal(so.cpu().numpy(), want_s)
+
+
+# Tiled MXFP4 / MXFP8 weights give the row-major layer bit for bit (the same products in the
+# same order), with bf16 and MXFP8 activations, 16-, 64- and 128-token tiles; intermediate 256
+# (the tiled order needs multiples of 256); and the tiled layer against the oracle once
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("act", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("T", [40, 600, 3000])
-def test_forward_tiny_mxfp4_tiled(act, T):
+def test_forward_tiny_block_tiled(wfmt, act, T):
     base = CONFIGS["tiny"].with_(moe_intermediate_size=256, shared_intermediate_size=256)
-    s = base.with_(weight_format="mxfp4", act_format=act)
+    s = base.with_(weight_format=wfmt, act_format=act)
+    quant = quantise_mxfp4 if wfmt == "mxfp4" else quantise_mxfp8
     bf = gen_experts(base, seed=25)
     ex = {}
     for k in ("gate", "up", "down"):
-        qs = [quantise_mxfp4(bf[k][e]) for e in range(s.E)]
+        qs = [quant(bf[k][e]) for e in range(s.E)]
         ex[k + "_q"] = np.stack([a for a, _ in qs])
         ex[k + "_s"] = np.stack([b for _, b in qs])
     c = host_case(s, seed=25, T=T, experts=ex)
     dev = DeviceCase(c)
     tiled = _tiled_case(dev)
-    say(f"[gpu] moe_forward tiny I=256 T={T} act={act}: tiled MXFP4 against row-major")
+    say(f"[gpu] moe_forward tiny I=256 T={T} {wfmt} act={act}: tiled against row-major")
     _assert_same_forward(dev, tiled)
     if T == 600:
-        check_forward(c, tol=TOL_MXFP4, dev=tiled)
+        check_forward(c, tol=TOL_BF16 if (wfmt, act) == ("mxfp8", "bf16") else TOL_MXFP4, dev=tiled)
 
 
 def test_quantise_mxfp8_bit_exact():
@@ -718,7 +743,9 @@ def test_forward_mxfp8_full(full_experts):
     with ThreadPoolExecutor(16) as pool:
         list(pool.map(q, range(E)))
     c = host_case(s, seed=0, experts=ex)
-    check_forward(c, rows=tile_rows(64), tol=TOL_BF16)
+    dev, _ = check_forward(c, rows=tile_rows(64), tol=TOL_BF16)
+    say("[gpu] the same layer with the experts in the tiled MXFP8 order: bit-exact")
+    _assert_same_forward(dev, _tiled_case(dev))
 
 
 @pytest.mark.slow
@@ -744,6 +771,5 @@ def test_forward_act_mxfp8_full(full_experts, wfmt):
         list(pool.map(q, range(E)))
     c = host_case(s, seed=0, experts=ex)
     dev, _ = check_forward(c, rows=tile_rows(64), tol=TOL_MXFP4)
-    if wfmt == "mxfp4":
-        say("[gpu] the same layer with the experts in the tiled MXFP4 order: bit-exact")
-        _assert_same_forward(dev, _tiled_case(dev))
+    say(f"[gpu] the same layer with the experts in the tiled {wfmt} order: bit-exact")
+    _assert_same_forward(dev, _tiled_case(dev))
