@@ -122,6 +122,14 @@ struct TStage {
   u32x4 t[NTP][CPT];
 };
 
+// bf16 planes of h the down GEMM reads: two (hi = bf16(h), lo = bf16(h - hi)) for bf16 and
+// MXFP8 expert weights, held to max|err| <= 2e-2 RMS; one for MXFP4 expert weights, held to
+// 5e-2 RMS (the rounding of h to bf16 alone measured at most 2.5e-2 RMS, on the tiny layouts
+// with few, large expert sums), which halves the down GEMM's h bytes and MFMAs
+template <int MODE, int WF> struct HPlanes {
+  static constexpr int value = MODE == MODE_GATEUP || WF == FMT_MXFP4 ? 1 : 2;
+};
+
 // One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
 // tile) are issued while step s computes, all in one batch, so that waiting for the token
 // tile of the next step (loads complete in issue order) never waits for younger weights.
@@ -129,7 +137,7 @@ template <int NW, int RF, int MF, int D, int MODE, int KS, int WF, bool PADDED>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                          int ksp, uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
-  constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;  // token planes (h hi and lo for down)
+  constexpr int NTP = HPlanes<MODE, WF>::value;  // token planes (down: h hi, and lo where kept)
   constexpr int BM = MF * 16;
   constexpr int SUB = KS / 32;       // MFMA sub-steps per step
   constexpr int LROW = KS + 16;      // LDS row stride (bf16); the 32-byte pad measured fewest bank conflicts
@@ -172,7 +180,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
       tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + k0 + col;
     } else {
       tsrc[0][i] = a.act + (size_t)(pos0 + prow) * K + k0 + col;
-      tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + k0 + col;
+      if constexpr (NTP == 2) tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + k0 + col;
     }
     tvalid[i] = ok;
   }
@@ -397,7 +405,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
               lv[r] = h - hv[r];  // exact in fp32
             }
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+            if constexpr (HPlanes<MODE_DOWN, WF>::value == 2)
+              *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
           } else if (a.ksplit > 1) {
             *(floatx4*)(a.part + ((size_t)ksp * a.T + pos0 + j) * N + ncol + f * 16) = acc[0][f][mf];
           } else if (a.out_bf16) {
@@ -918,7 +927,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FfnMinW
 void ffn_kernel(FfnArgs a) {
   constexpr bool PADDED = FMT != FMT_BF16 || MF >= 4;
   constexpr int BM = MF * 16;
-  constexpr int NTP = MODE == MODE_GATEUP ? 1 : 2;
+  constexpr int NTP = HPlanes<MODE, FMT>::value;
   // bf16 token planes (double-buffered, rows padded by 32 bytes), or for MXFP8 activations a
   // ring of D + 1 stages of codes and scale words
   constexpr int LDS_BYTES = ACT == ACT_MXFP8 ? (D + 1) * (BM * KS + (KS / 128) * ((BM + 63) / 64 * 64) * 4)
@@ -1020,15 +1029,13 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 // (KS_ALT, D_ALT).
 // MXFP8 activations (ACT_MXFP8): 4 waves of two 16-row blocks each (gate/up rounds h in
 // blocks of 32 rows of one wave), 128-value steps.
-// RFW > 0 sets the weight row blocks per wave (the block-format, bf16-activation down GEMM on
-// 32-token tiles takes 4: each h stage then serves 256 weight rows)
-template <int MF, int FMT, int MODE, int ACT = ACT_BF16, int RFW = 0> struct FfnCfg {
+template <int MF, int FMT, int MODE, int ACT = ACT_BF16> struct FfnCfg {
   static constexpr bool FP4 = FMT != FMT_BF16;  // MX weights (MXFP4 or MXFP8): 128-value steps
   static constexpr bool A8 = ACT == ACT_MXFP8;
   static constexpr bool DOWN = MODE == MODE_DOWN;
   static constexpr bool WIDE = !FP4 && (MF == 1 || (MF == 2 && !DOWN));
   static constexpr int NW = (MF <= 2 || DOWN || A8) ? 4 : 8;
-  static constexpr int RF = RFW ? RFW : WIDE ? 1 : (MF <= 2 || DOWN || A8) ? 2 : 1;
+  static constexpr int RF = WIDE ? 1 : (MF <= 2 || DOWN || A8) ? 2 : 1;
   static constexpr int KS = A8 ? 256 : FP4 ? 128 : WIDE ? ((MF == 1 && DOWN) ? 384 : 256) : 64;
   // MXFP8 activations: 256-value steps where K allows (128 otherwise), tokens in an LDS ring
   // (no registers), weights D steps ahead in registers
@@ -1042,9 +1049,9 @@ template <int MF, int FMT, int MODE, int ACT = ACT_BF16, int RFW = 0> struct Ffn
   static constexpr int KS_ALT = (WIDE || A8) ? 128 : KS, D_ALT = WIDE ? 4 : D;
 };
 
-template <int MF, int MODE, int FMT, int ACT = ACT_BF16, int RFW = 0>
+template <int MF, int MODE, int FMT, int ACT = ACT_BF16>
 hipError_t launch_one(FfnArgs a, int rbw, int64_t max_tiles, hipStream_t s, Tracer* tr, const char* name = nullptr) {
-  using C = FfnCfg<MF, FMT, MODE, ACT, RFW>;
+  using C = FfnCfg<MF, FMT, MODE, ACT>;
   if (ACT == ACT_MXFP8 && (a.ksplit != 1 || a.dense)) return hipErrorInvalidValue;
   constexpr int ROWS = C::NW * C::RF * 16;  // weight rows per block of each matrix
   if (a.bm_list % (16 * MF) || a.N % ROWS || a.ksplit < 1 || a.K % a.ksplit) return hipErrorInvalidValue;
@@ -1088,12 +1095,6 @@ hipError_t launch_mode(int mf, const FfnArgs& a, int rbw, int fmt, int64_t max_t
 #undef MOE_A8
     return hipErrorInvalidValue;  // MXFP8 activations need block-format weights
   }
-  // MXFP4 weights, bf16 activations: the down GEMM on 32-token tiles with four 16-row blocks
-  // per wave where H allows (measured at 4096 tokens: 0.427 ms with 64-token tiles and two
-  // blocks per wave, 0.403 with 32-token tiles and two, 0.393 with four; MXFP8 weights, whose
-  // stage is twice the bytes, were slower so: 0.478 -> 0.557 ms)
-  if (MODE == MODE_DOWN && mf == 2 && fmt == FMT_MXFP4 && a.N % 256 == 0)
-    return launch_one<2, MODE, FMT_MXFP4, ACT_BF16, 4>(a, rbw, max_tiles, s, tr);
   if (fmt == FMT_MXFP4) {
     switch (mf) {
       case 1: return launch_one<1, MODE, FMT_MXFP4>(a, rbw, max_tiles, s, tr);
@@ -1280,13 +1281,11 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
     err = launch_mode<MODE_GATEUP>(sp.mf, gu_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_gate_up_shared");
     if (err != hipSuccess) return err;
   }
-  // MXFP4 weights with bf16 activations: the down GEMM takes 32-token sub-tiles (two bf16 h
-  // planes per token make the h stage the larger operand; 256-row blocks where H allows, so
-  // the same rows per workgroup in half the blocks)
-  const bool dn32 = !a8 && w.fmt == FMT_MXFP4;
-  const int mf_dn = dn32 ? std::min(p.mf_down, 2) : p.mf_down;
-  const int rbw_dn = dn32 && p.mf_down >= 2 && H % 256 == 0 ? std::max(1, p.rbw_down / 2) : p.rbw_down;
-  err = launch_mode<MODE_DOWN>(mf_dn, dn, rbw_dn, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
+  // (MXFP4 weights with bf16 activations read one h plane, so their down GEMM keeps the
+  // plan's tiles: measured at 4096 tokens, 0.270 ms with 64-token tiles against 0.304 with
+  // 32-token ones, and 0.312 with 32-token tiles of four 16-row blocks per wave, the shape that
+  // was fastest with two planes)
+  err = launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess || !S) return err;
   dn_s.act = h_hi + pos * I; dn_s.act_lo = h_lo + pos * I;
   dn_s.w0 = w.sh_down; dn_s.s0 = nullptr;
