@@ -631,11 +631,12 @@ def profile_commands(workload: str, out: str = "$OUT"):
             f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/fetch -o fetch -- {b}",
             f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/write -o write -- {b}",
             f"rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict -f csv -d {out}/util -o util -- {b}",
+            f"rocprofv3 --pmc VmemLatency -f csv -d {out}/lat -o lat -- {b}",
             f"python3 $R/bench.py --summarize {out} --workload {workload}"]
 
 
 def summarize(src: str, workload: str):
-    """Turn the three rocprofv3 runs of profile_commands() into profiles/<kernel>_<workload>.md
+    """Turn the rocprofv3 runs of profile_commands() into profiles/<kernel>_<workload>.md
     and the workload's entry in profiles/traffic.json (HBM bytes per launch of each step, with
     the kernel-source hash they were taken on)."""
     import csv
@@ -662,6 +663,9 @@ def summarize(src: str, workload: str):
     util_f = glob.glob(os.path.join(src, "util/*counter_collection.csv"))
     util = {n: counters(util_f[0], n) for n in ("MfmaUtil", "VALUBusy", "LdsUtil", "LdsBankConflict")} \
         if util_f else {}
+    lat_f = glob.glob(os.path.join(src, "lat/*counter_collection.csv"))
+    if lat_f:
+        util["VmemLatency"] = counters(lat_f[0], "VmemLatency")
     copy_f, copy_w = max(fetch["__amd_rocclr_copyBuffer"]), max(write["__amd_rocclr_copyBuffer"])
     sf, sw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
     steps = {}
@@ -697,15 +701,19 @@ def summarize(src: str, workload: str):
     for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
         lines.append(f"| {st} | `{e['symbol']}` | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} |")
     if util:
-        lines += ["", "## Utilisation per launch (rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict)", "",
+        lines += ["", "## Utilisation per launch (rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict; "
+                  "then VmemLatency)", "",
                   "MfmaUtil = MFMA busy cycles / (GPU cycles x SIMDs) in %; VALUBusy = VALU instruction cycles "
                   "per CU in %; LdsUtil = LDS busy cycles per CU in %; LdsBankConflict = conflict cycles per "
-                  "conflict-free LDS cycle.", "",
-                  "| step | MfmaUtil % | VALUBusy % | LdsUtil % | LdsBankConflict |", "|---|---|---|---|---|"]
+                  "conflict-free LDS cycle; VmemLatency = mean cycles a vector memory instruction is in flight "
+                  "(issue to completion).", "",
+                  "| step | MfmaUtil % | VALUBusy % | LdsUtil % | LdsBankConflict | VmemLatency cycles |",
+                  "|---|---|---|---|---|---|"]
         for st, e in sorted(steps.items(), key=lambda kv: -kv[1]["avg_us"]):
             u = e["util"]
             lines.append(f"| {st} | {u.get('MfmaUtil', float('nan')):.1f} | {u.get('VALUBusy', float('nan')):.1f} | "
-                         f"{u.get('LdsUtil', float('nan')):.1f} | {u.get('LdsBankConflict', float('nan')):.3f} |")
+                         f"{u.get('LdsUtil', float('nan')):.1f} | {u.get('LdsBankConflict', float('nan')):.3f} | "
+                         f"{u.get('VmemLatency', float('nan')):.0f} |")
     os.makedirs(PROFILES, exist_ok=True)
     md = os.path.join(PROFILES, f"{dom}_{workload}_T{shape.T}.md")
     with open(md, "w") as fh:
