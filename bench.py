@@ -214,12 +214,27 @@ def measure(shape, d, steps, warmup, hip):
         hip.record(marks[s + 1], stream)
     torch.cuda.synchronize()
     step_ms = np.array([hip.elapsed_ms(marks[s], marks[s + 1]) for s in range(steps)])
+    # cold caches, outside the timed region: before each step a 512 MB buffer is read (twice
+    # the 256 MB Infinity Cache, so no weight byte of the previous step is still cached; read,
+    # not written, so that no dirty lines are written back during the step), then the step
+    # runs between two events
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    cold = [(hip.event(), hip.event()) for _ in range(steps)]
+    for s in range(steps):
+        torch.amax(flush, dim=0, out=sink)
+        hip.record(cold[s][0], stream)
+        moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, None, None, None, ws)
+        hip.record(cold[s][1], stream)
+    torch.cuda.synchronize()
+    cold_ms = [hip.elapsed_ms(a, b) for a, b in cold]
+    del flush, sink
     # routing of the last step (for algorithmic bytes)
     moe.moe_forward(cfg, T, d["x"], d["router_w"], d["bias"], d["weights"], out, idx, wts, cnt, ws)
     torch.cuda.synchronize()
     counts = cnt.cpu().numpy()
     return dict(wall_ms=wall_ms, event_ms=ev_ms, kernels=kmean, dom=dom, dom_ms=dom_ms, counts=counts, out=out,
-                idx=idx.cpu().numpy(), dom_dist=_dist(dom_all), step_dist=_dist(step_ms))
+                idx=idx.cpu().numpy(), dom_dist=_dist(dom_all), step_dist=_dist(step_ms), cold_dist=_dist(cold_ms))
 
 
 def _dist(v):
@@ -500,7 +515,18 @@ def layer_summary(shape, r, measured=None):
                 binding_roofline_frac=round(max(hbm_t, mfma_t) / (ms * 1e-3), 4),
                 hbm_frac_of_measured_read=round(byts / (ms * 1e-3) / 1e9 / measured["read_GBps"], 4) if measured else None,
                 router_fp32_flops=2.0 * T * H * E, touched_experts=touched, step_ms_dist=r.get("step_dist"),
-                load=load_stats(shape, counts))
+                cold=cold_summary(shape, r), load=load_stats(shape, counts))
+
+
+def cold_summary(shape, r):
+    """The step with cold caches (a 512 MB read before each step, outside the events): median
+    and spread of the step, its tokens/s, and its fraction of the HBM peak on the same
+    algorithmic bytes as the warm figure."""
+    cd = r.get("cold_dist")
+    if not cd:
+        return None
+    return {"step_ms_dist": cd, "value": round(shape.T / (cd["median"] * 1e-3), 1), "unit": "tokens/s",
+            "note": "512 MB read between steps (twice the Infinity Cache); one event pair per step"}
 
 
 def library_gemm(shape, d, idx, hip, reps=10):
