@@ -415,14 +415,15 @@ def roofline(shape, r, workload=None, measured=None):
     if measured:
         # HBM-bound kernels here mostly read: the measured read rate is their ceiling
         rl["frac_of_measured"] = round(gbs / measured["read_GBps"], 4) if rl["bound"] == "hbm" else \
-            round(tflops / measured["bf16_mfma_TFLOPs"], 4)
+            round(tflops / measured["fp8_mfma_TFLOPs" if mfma_peak(shape) == FP8_PEAK_TFLOPS else "bf16_mfma_TFLOPs"], 4)
     return rl
 
 
 def measured_peaks(hip, nbytes=1 << 30, n=4096):
     """Achievable rates on this GPU, beside the nominal peaks, from the probe kernels of
     libmoe_probe.so (package/probe/peak_probe.hip): a plain 1 GiB HBM read, a plain 1 GiB copy
-    (bytes read + written) and a loop of independent bf16 16x16x32 MFMAs, each the best over
+    (bytes read + written) and loops of independent MFMAs (bf16 16x16x32; scaled 16x16x128 on
+    E4M3 and on E2M1 operands), each the best over
     a few grid sizes and 3 runs, timed with events; plus torch's bf16 GEMM (hipBLASLt) at
     n x n x n as a library reference."""
     import torch
@@ -449,13 +450,19 @@ def measured_peaks(hip, nbytes=1 << 30, n=4096):
     grids = (1024, 2048, 4096, 8192, 16384)
     t_read = best(lambda g: lib.moe_probe_read(V(a.data_ptr()), S(n16), V(sink.data_ptr()), I(g), V(stream)), grids)
     t_copy = best(lambda g: lib.moe_probe_copy(V(a.data_ptr()), V(b.data_ptr()), S(n16), I(g), V(stream)), grids)
-    iters = 2000
-    t_mfma, g_mfma = 1e9, 0
-    for g in (512, 1024, 2048):
-        t = best(lambda gg: lib.moe_probe_mfma_bf16(I(iters), I(gg), V(sink.data_ptr()), V(stream)), (g,))
-        if g * 4 * iters * 8 * 16384 * 2 / t > g_mfma * 4 * iters * 8 * 16384 * 2 / max(t_mfma, 1e-9):
-            t_mfma, g_mfma = t, g
-    mfma_tflops = g_mfma * 4 * iters * 8 * 16384 * 2.0 / (t_mfma * 1e-3) / 1e12
+    # MFMA loops: grid workgroups of 4 waves, `chains` independent MFMAs per wave and iteration
+    iters, chains = 1000, lib.moe_probe_mfma_chains()
+
+    def mfma_rate(launch, flops_per_mfma):
+        rate = 0.0
+        for g in (1024, 2048, 4096):
+            t = best(lambda gg: launch(gg), (g,))
+            rate = max(rate, g * 4 * iters * chains * flops_per_mfma / (t * 1e-3) / 1e12)
+        return rate
+    sp = V(sink.data_ptr())
+    mfma_tflops = mfma_rate(lambda g: lib.moe_probe_mfma_bf16(I(iters), I(g), sp, V(stream)), 2 * 16 * 16 * 32)
+    fp8_tflops = mfma_rate(lambda g: lib.moe_probe_mfma_scaled(I(0), I(iters), I(g), sp, V(stream)), 2 * 16 * 16 * 128)
+    fp4_tflops = mfma_rate(lambda g: lib.moe_probe_mfma_scaled(I(4), I(iters), I(g), sp, V(stream)), 2 * 16 * 16 * 128)
     A = torch.randn((n, n), device="cuda").to(torch.bfloat16)
     B = torch.randn((n, n), device="cuda").to(torch.bfloat16)
     C = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
@@ -464,9 +471,12 @@ def measured_peaks(hip, nbytes=1 << 30, n=4096):
     return {"read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
             "copy_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
             "bf16_mfma_TFLOPs": round(mfma_tflops, 1),
+            "fp8_mfma_TFLOPs": round(fp8_tflops, 1),
+            "fp4_mfma_TFLOPs": round(fp4_tflops, 1),
             "bf16_gemm_TFLOPs": round(2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, 1),
-            "note": "probe kernels (1 GiB read; 1 GiB copy, read + written bytes; independent bf16 MFMA loop) "
-                    "and torch bf16 matmul 4096^3 (hipBLASLt); best over grids and runs"}
+            "note": "probe kernels (1 GiB read; 1 GiB copy, read + written bytes; loops of independent bf16 "
+                    "16x16x32 MFMAs and of scaled 16x16x128 MFMAs on E4M3 and E2M1 operands) and torch bf16 matmul "
+                    "4096^3 (hipBLASLt); best over grids and runs"}
 
 
 def layout_probe(hip, rows=225 * 1536, K=2560, reps=5):
@@ -613,13 +623,29 @@ def cpu_baseline(shape, d, experts, max_tokens):
                          act_quant="mxfp8" if shape.act_format == "mxfp8" else "none")
         dt += time.perf_counter() - t0
         passes += 1
+    # routing alone (logits, sigmoid, grouped top-k, weights) on the same sample
+    rpasses, rdt = 0, 0.0
+    while rpasses == 0 or (rdt < 2.0 and rpasses < 200):
+        t0 = time.perf_counter()
+        oracle.route(oracle.router_logits(x, d["router_w_np"]), d["bias_np"], n_group=shape.G,
+                     topk_group=shape.TG, top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
+                     norm_topk_prob=shape.norm_topk_prob)
+        rdt += time.perf_counter() - t0
+        rpasses += 1
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=round(T * passes / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"float64 oracle forward of the first {T} tokens of the {shape.name} workload "
-                       f"(H{shape.H}/E{shape.E}/top{shape.K}), {passes} passes, {dt:.1f} s")
+                       f"(H{shape.H}/E{shape.E}/top{shape.K}), {passes} passes, {dt:.1f} s",
+                routing_only_value=round(T * rpasses / rdt, 1), cpu_model=model)
 
 
 # ----------------------------------------------------------------------------------

@@ -48,23 +48,47 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
   for (; i < n; i += stride) dst[i] = src[i];
 }
 
-// `iters` rounds of 8 independent 16x16x32 bf16 MFMAs per wave (operands from the lane id,
-// so nothing folds); one float per workgroup is written only if the sum equals a value it
-// never takes in practice
+// `iters` rounds of NACC independent 16x16x32 bf16 MFMAs per wave (operands from the lane id,
+// so nothing folds; measured at 4096 workgroups: 8 chains 1.47, 16 chains 2.06, 32 chains 2.16
+// PFLOP/s, so fewer chains are latency-bound); one float per workgroup is written only if the
+// sum equals a value it never takes in practice
+constexpr int PROBE_NACC = 32;
 __global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* __restrict__ sink) {
   const uint32_t l = threadIdx.x;
   const u32x4 ab = {0x3F803F80u ^ (l & 7u), 0x3F003F00u ^ (l & 3u), 0x3E803E80u, 0x3F803F80u};
   const bf16x8 a = __builtin_bit_cast(bf16x8, ab);
-  floatx4 acc[8];
+  floatx4 acc[PROBE_NACC];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, (float)j};
+  for (int j = 0; j < PROBE_NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, (float)j};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[j], 0, 0, 0);
+    for (int j = 0; j < PROBE_NACC; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[j], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  for (int j = 0; j < PROBE_NACC; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+// The same loop on the scaled MFMA, 16x16x128 with both operands in FMT (0 = E4M3, 4 = E2M1,
+// whose operand uses the low four dwords) and unit block scales (e8m0 127)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <int FMT>
+__global__ __launch_bounds__(256) void mfma_scale_kernel(int iters, float* __restrict__ sink) {
+  const int l = (int)threadIdx.x;
+  const i32x8 a = {0x38383838 ^ (l & 7), 0x30303030 ^ (l & 3), 0x34343434, 0x38383838,
+                   0x38383838, 0x30303030, 0x34343434 ^ (l & 1), 0x38383838};
+  floatx4 acc[PROBE_NACC];
+#pragma unroll
+  for (int j = 0; j < PROBE_NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, (float)j};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < PROBE_NACC; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, a, acc[j], FMT, FMT, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < PROBE_NACC; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
   if (s == -1234.5f) sink[blockIdx.x] = s;
 }
 
@@ -127,11 +151,25 @@ int moe_probe_copy(const void* src, void* dst, size_t n16, int grid, void* strea
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-// grid workgroups of 4 waves, each wave 8 * iters bf16 MFMAs of 16x16x32 (16384 flops each);
-// sink: device, >= grid floats
+// independent MFMA chains per wave of the probes below
+int moe_probe_mfma_chains(void) { return PROBE_NACC; }
+
+// grid workgroups of 4 waves, each wave PROBE_NACC * iters bf16 MFMAs of 16x16x32 (2*16*16*32
+// = 16384 flops each); sink: device, >= grid floats
 int moe_probe_mfma_bf16(int iters, int grid, void* sink, void* stream) {
   if (!sink || grid <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_bf16_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, (float*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// the same with scaled MFMAs of 16x16x128 (65536 flops each) on E4M3 (fmt 0) or E2M1 (fmt 4)
+// operands
+int moe_probe_mfma_scaled(int fmt, int iters, int grid, void* sink, void* stream) {
+  if (!sink || grid <= 0 || iters <= 0 || (fmt != 0 && fmt != 4)) return -1;
+  if (fmt == 0)
+    hipLaunchKernelGGL(mfma_scale_kernel<0>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, (float*)sink);
+  else
+    hipLaunchKernelGGL(mfma_scale_kernel<4>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, (float*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
