@@ -249,8 +249,12 @@ def load_stats(shape, counts):
     workload is built so that it exceeds one half)."""
     c = np.sort(np.asarray(counts[:shape.E], np.int64))[::-1]
     total = int(c.sum())
+    p = c[c > 0] / max(1, total)
+    # routing entropy -sum p log p of the assignment shares, in nats (a diagnostic; a uniform
+    # spread over the experts gives log E)
     return {"touched_experts": int((c > 0).sum()), "max_count": int(c[0]), "mean_count": round(total / shape.E, 2),
-            "top10pct_share": round(float(c[: max(1, shape.E // 10)].sum()) / max(1, total), 4)}
+            "top10pct_share": round(float(c[: max(1, shape.E // 10)].sum()) / max(1, total), 4),
+            "entropy_nats": round(float(-(p * np.log(p)).sum()), 3), "entropy_uniform_nats": round(float(np.log(shape.E)), 3)}
 
 
 def time_bias_update(shape, counts, hip, reps=200):
@@ -600,6 +604,47 @@ def routing_check(shape, d, idx_gpu):
             "differ_elsewhere": int((diff & ~r.near_tie).sum()), "tie_eps": 1e-6}
 
 
+def check_rows(T, n=16):
+    """Rows of the output the benchmark compares with the oracle: the first, the last and
+    evenly spaced ones in between."""
+    return np.unique(np.linspace(0, T - 1, n).round().astype(np.int64))
+
+
+def sampled_output(shape, out):
+    """The bf16 bits of the sampled rows of a step's output, copied to the host."""
+    import torch
+    rows = torch.from_numpy(check_rows(shape.T)).to(out.device)
+    return out.index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def output_check(shape, d, experts, got_bits):
+    """The float64 oracle forward of the sampled rows (part of the CPU leg) against the GPU's
+    rows: max|err| / RMS(oracle) over the rows whose routing has no near tie, beside the bar
+    (2e-2 for bf16 and MXFP8 weights, 5e-2 for MXFP4 weights and for MXFP8 activations)."""
+    import oracle
+    rows = check_rows(shape.T)
+    x = oracle.bf16_to_f64(d["x_bits"][rows])
+
+    def get(e):
+        if shape.weight_format in ("mxfp4", "mxfp8"):
+            dq = oracle.mxfp4_dequant if shape.weight_format == "mxfp4" else oracle.mxfp8_dequant
+            return tuple(dq(experts[k + "_q"][e], experts[k + "_s"][e]) for k in ("gate", "up", "down"))
+        return tuple(oracle.bf16_to_f64(experts[k][e]) for k in ("gate", "up", "down"))
+    sh = tuple(oracle.bf16_to_f64(d["shared_np"][k]) for k in ("gate", "up", "down"))
+    ref, r = oracle.moe_layer(x, d["router_w_np"], d["bias_np"], get, sh, n_group=shape.G, topk_group=shape.TG,
+                              top_k=shape.K, routed_scaling_factor=shape.routed_scaling_factor,
+                              norm_topk_prob=shape.norm_topk_prob, swiglu_limit=shape.swiglu_limit,
+                              shared_swiglu_limit=shape.shared_swiglu_limit,
+                              act_quant="mxfp8" if shape.act_format == "mxfp8" else "none")
+    got = oracle.bf16_to_f64(got_bits)
+    keep = ~r.near_tie
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.abs(got - ref)[keep].max()) if keep.any() else 0.0
+    bar = 5e-2 if (shape.weight_format == "mxfp4" or shape.act_format == "mxfp8") else 2e-2
+    return {"rows": int(len(rows)), "near_tie_rows": int((~keep).sum()), "max_abs_err_over_rms": round(err / rms, 5),
+            "bar": bar}
+
+
 def cpu_baseline(shape, d, experts, max_tokens):
     """The float64 oracle on the host cores, on the first `max_tokens` tokens of the workload."""
     import oracle
@@ -898,8 +943,9 @@ def main():
         line["layout_probe"] = layout_probe(hip)
     if args.library_gemm and shape.weight_format == "bf16":
         line["library_gemm"] = library_gemm(shape, d, r["idx"], hip)
-    host = ("x_bits", "router_w_np", "bias_np")
+    host = ("x_bits", "router_w_np", "bias_np", "shared_np")
     checks = [(shape, {k: d[k] for k in host}, r["idx"])]
+    outs = {shape.name: (experts, sampled_output(shape, r["out"]))}
     if not args.no_secondary and shape.name == "decode":
         # the other workloads on the same layer: prefill (the metric's T=8192), skewed routing
         # with the deep-layer clamp, and the routed experts in MXFP4 (quantised from the same
@@ -944,6 +990,7 @@ def main():
                 "roofline": roofline(p, rp, measured=measured), "layer": layer_summary(p, rp, measured),
                 "kernels_ms": {k: round(v, 4) for k, v in rp["kernels"].items()}}
             checks.append((p, {k: dp[k] for k in host}, rp["idx"]))
+            outs[name] = (ex, sampled_output(p, rp["out"]))
             del dp
             torch.cuda.empty_cache()
         line["prefill"] = line["secondary"]["prefill"]
@@ -952,6 +999,8 @@ def main():
         line["cpu_baseline"] = cpu_baseline(shape, d, experts, args.cpu_tokens)
         # the oracle's routing of every measured step, beside the GPU's
         line["routing_check"] = {c[0].name: routing_check(*c) for c in checks}
+        log("checking sampled output rows against the oracle ...")
+        line["output_check"] = {c[0].name: output_check(c[0], c[1], *outs[c[0].name]) for c in checks}
     print(json.dumps(line), flush=True)
 
 

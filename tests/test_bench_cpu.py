@@ -78,3 +78,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "single MI355X" in r.stderr
+
+
+def test_output_check_measures_against_the_oracle():
+    """The benchmark's sampled output check: rows equal to the oracle's rounded to bf16 sit
+    below the bar (the output's own bf16 rounding costs ~1.4 % of RMS), and a planted error in
+    one row is reported at its size."""
+    import numpy as np
+    import oracle
+    from synthetic import CONFIGS, gen_bias, gen_experts, gen_router, gen_shared, gen_x
+    s = CONFIGS["tiny"].with_(T=100)
+    d = dict(x_bits=gen_x(s, 0), router_w_np=gen_router(s), bias_np=gen_bias(s), shared_np=gen_shared(s))
+    ex = gen_experts(s)
+    rows = bench.check_rows(s.T)
+    assert rows[0] == 0 and rows[-1] == s.T - 1 and len(rows) == 16
+    ref, _ = oracle.moe_layer(oracle.bf16_to_f64(d["x_bits"][rows]), d["router_w_np"], d["bias_np"],
+                              lambda e: tuple(oracle.bf16_to_f64(ex[k][e]) for k in ("gate", "up", "down")),
+                              tuple(oracle.bf16_to_f64(d["shared_np"][k]) for k in ("gate", "up", "down")),
+                              n_group=s.G, topk_group=s.TG, top_k=s.K)
+    bits = (np.round(ref.astype(np.float32).view(np.uint32) / 65536.0)).astype(np.uint32).astype(np.uint16)
+    ok = bench.output_check(s, d, ex, bits)
+    assert ok["rows"] == 16 and ok["bar"] == 2e-2 and ok["max_abs_err_over_rms"] < 2e-2
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bad = ref.copy()
+    bad[3, 7] += 0.1 * rms
+    bad_bits = (np.round(bad.astype(np.float32).view(np.uint32) / 65536.0)).astype(np.uint32).astype(np.uint16)
+    assert abs(bench.output_check(s, d, ex, bad_bits)["max_abs_err_over_rms"] - 0.1) < 0.02
