@@ -18,7 +18,11 @@
 //     tokens: vector memory loads complete in issue order;
 //   * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by (row >> 1) & 7, which
 //     keeps the MFMA fragment reads free of bank conflicts;
-//   * MFMA sub-step u takes k = 32u + 8q .. +7 for lane group q in both operands.
+//   * MFMA sub-step u takes k = 32u + 8q .. +7 for lane group q in both operands;
+//   * the SwiGLU activation h passes from gate/up to down as one fp16 plane (11 significant
+//     bits, where the few-token kernels keep two bf16 planes): the down GEMM converts each
+//     bf16 weight fragment to fp16 in registers (exact for these weights) and multiplies on
+//     the fp16 MFMA, at the bf16 rate, so h costs half the bytes and half the MFMAs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -33,8 +37,7 @@ constexpr int T_ROWB = T_KS * 2;   // bytes of one row (weight or token) per sta
 constexpr int T_LIST_BM = 256;     // positions per tile of the device tile list
 
 struct TileArgs {
-  const uint16_t* act;          // gate/up: x [T,K]; down: h hi plane [P,K]
-  const uint16_t* act_lo;       // down: h lo plane [P,K]
+  const uint16_t* act;          // gate/up: x [T,K] bf16; down: h [P,K] fp16
   const int32_t* sorted_token;  // gate/up: token of each sorted position
   const int32_t* offsets;       // [E+2]
   const int32_t* tile_prefix;   // [E+2] tiles of 256 positions before expert e
@@ -42,8 +45,7 @@ struct TileArgs {
   const uint16_t* w1;           // routed up (gate/up)
   const uint16_t* sw0;          // shared expert gate or down
   const uint16_t* sw1;          // shared expert up
-  void* out;                    // gate/up: h hi plane bf16 [P,N]; down: y fp32 [P,N]
-  uint16_t* out_lo;             // gate/up: h lo plane
+  void* out;                    // gate/up: h fp16 [P,N]; down: y fp32 [P,N]
   int T, E, S;
   int K, N;                     // reduction length, output columns per expert
   int nrb;                      // row blocks per expert (N / rows of one block)
@@ -67,6 +69,28 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l_base) {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// two fp32 -> two fp16, round to nearest even, low half first
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// eight bf16 -> eight fp16: exact for magnitudes from 2^-17 (fp16 keeps the 8 significant bits
+// of bf16 down to there) up to 65504; smaller ones lose low bits toward zero (an absolute
+// error below 2^-24), larger ones (never bf16 model weights) become infinite
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                                                     __uint_as_float(w[i] & 0xFFFF0000u)));
+  return r;
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma16_f16(const u32x4& a, const u32x4& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // vmcnt wait with a compile-time count (other counters left alone)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -82,7 +106,7 @@ typedef const __attribute__((address_space(4))) int32_t* sptr;
 template <int MODE, int RFR, int TPW, int NSTAGE>
 __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
   constexpr int NMAT = MODE == TM_GATEUP ? 2 : 1;
-  constexpr int NTP = MODE == TM_GATEUP ? 1 : 2;
+  constexpr int NTP = 1;  // token planes: x (gate/up) or the fp16 h (down)
   constexpr int BM = T_NW * TPW * 16;              // positions per work item
   constexpr int WROWS = NMAT * RFR * 16;           // weight rows per stage
   constexpr int W_BYTES = WROWS * T_ROWB;
@@ -194,9 +218,7 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
         tsrc[0][tf] = a.act + (size_t)(ok ? tok : 0) * K + q * 8;
       } else {
         tok_new[tf] = true;
-        const size_t row = (size_t)(it.pos0 + (j < it.nrows ? j : 0)) * K + q * 8;
-        tsrc[0][tf] = a.act + row;
-        tsrc[NTP - 1][tf] = a.act_lo + row;
+        tsrc[0][tf] = a.act + (size_t)(it.pos0 + (j < it.nrows ? j : 0)) * K + q * 8;
       }
     }
   };
@@ -264,7 +286,7 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
   // compiler from sinking those reads next to their use, so the LDS latency overlaps the
   // MFMAs of the fragments before.
   constexpr int NF = NMAT * RFR;
-  constexpr int FPF = NTP * TPW >= 4 ? 4 : 8;  // ~256 MFMA cycles between a read and its use
+  constexpr int FPF = 8;  // ~256 MFMA cycles between a read and its use
   auto compute = [&](int g, const u32x4 (&tv)[NTP][TPW][2]) {
     const uint8_t* st = lds + (g % NSTAGE) * W_BYTES;
     auto frag = [&](int idx) {
@@ -281,11 +303,15 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const int u = idx / NF, fi = idx - u * NF;
       const int m = fi / RFR, f = fi - m * RFR;
+      if constexpr (MODE == TM_GATEUP) {
 #pragma unroll
-      for (int p = NTP - 1; p >= 0; --p)
+        for (int tf = 0; tf < TPW; ++tf) acc[m][f][tf] = mfma16(wf[idx % (FPF + 1)], tv[0][tf][u], acc[m][f][tf]);
+      } else {
+        // down: the bf16 weights as fp16 (exact from 2^-17 up), against the fp16 h
+        const u32x4 wh = bf16x8_to_f16x8(wf[idx % (FPF + 1)]);
 #pragma unroll
-        for (int tf = 0; tf < TPW; ++tf)
-          acc[m][f][tf] = mfma16(wf[idx % (FPF + 1)], tv[p][tf][u], acc[m][f][tf]);
+        for (int tf = 0; tf < TPW; ++tf) acc[m][f][tf] = mfma16_f16(wh, tv[0][tf][u], acc[m][f][tf]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -301,18 +327,18 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int f = 0; f < RFR; ++f) {
           if (MODE == TM_GATEUP) {
-            float hv[4], lv[4];
+            // h in fp16, one plane: 11 significant bits (bf16 keeps 8); saturated at the fp16
+            // maximum, which the clamp of the deep layers and these activations stay far below
+            float hv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float g = acc[0][f][tf][r], uu = acc[NMAT - 1][f][tf][r];
               float h = g / (1.0f + __expf(-g)) * uu;
               if (limit > 0.f) h = fminf(fmaxf(h, -limit), limit);
               if (!tok_ok[tf]) h = 0.f;
-              hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
-              lv[r] = h - hv[r];  // exact in fp32
+              hv[r] = fminf(fmaxf(h, -65504.f), 65504.f);
             }
-            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_f16x2(hv[0], hv[1]), pack_f16x2(hv[2], hv[3])};
           } else {
             *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][tf];
           }
@@ -423,7 +449,7 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
   gu.w0 = (const uint16_t*)w.gate; gu.w1 = (const uint16_t*)w.up;
   gu.sw0 = (const uint16_t*)w.sh_gate; gu.sw1 = (const uint16_t*)w.sh_up;
-  gu.out = h_hi; gu.out_lo = h_lo;
+  gu.out = h_hi;  // h as one fp16 plane (h_lo is not used by these kernels)
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
   // one weight set (a dense FFN): one row block per item, for twice the items (a single
   // expert has few token tiles to spread over the CUs)
@@ -435,9 +461,9 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   gu.interleave = GU_INTERLEAVE;
 
   TileArgs dn = gu;
-  dn.act = h_hi; dn.act_lo = h_lo; dn.sorted_token = nullptr;
+  dn.act = h_hi; dn.sorted_token = nullptr;
   dn.w0 = (const uint16_t*)w.down; dn.w1 = nullptr; dn.sw0 = (const uint16_t*)w.sh_down; dn.sw1 = nullptr;
-  dn.out = y; dn.out_lo = nullptr;
+  dn.out = y;
   dn.K = I; dn.N = H;
   dn.interleave = DN_INTERLEAVE;
   dn.nrb = H / (DN_RFR * 16); dn.rbw = std::min(dn.nrb, single ? 1 : DN_RBW);
