@@ -1203,7 +1203,8 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                              int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
                              float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
-                             bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab) {
+                             bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab, bool own_shared,
+                             hipStream_t shared_s) {
   hipError_t err = hipSuccess;
   const bool a8 = ab && ab->act == ACT_MXFP8;
   if (a8 && (p.tiles || w.fmt == FMT_BF16 || !ab->xq || !ab->xs || !ab->hq || !ab->hs)) return hipErrorInvalidValue;
@@ -1257,7 +1258,10 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   // scaled-MFMA ones), restricted to their tiles, so that they carry no bf16-weight registers;
   // the shared expert (bf16 weights and activations) on the bf16 kernels as a dense FFN over
   // all T tokens, whose block of sorted positions is the identity at T*K (so its tile size
-  // follows from T, not from the routed experts' tokens)
+  // follows from T, not from the routed experts' tokens).  It reads x only, so the caller may
+  // give it a stream of its own (own_shared, shared_s) that runs beside the routing and the
+  // routed experts; the launches keep their order in the tracer's count either way.
+  const hipStream_t ss = own_shared ? shared_s : s;
   const int act = a8 ? ACT_MXFP8 : ACT_BF16;
   FfnArgs gu_s = gu, dn_s = dn;
   if (a8) {
@@ -1278,7 +1282,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
     gu_s.out = h_hi + pos * I; gu_s.out_lo = h_lo + pos * I;
     gu_s.E = 1; gu_s.S = 0; gu_s.limit = shared_limit;
     gu_s.dense = 1; gu_s.bm_list = 16 * sp.mf; gu_s.group_major = sp.group_major;
-    err = launch_mode<MODE_GATEUP>(sp.mf, gu_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_gate_up_shared");
+    err = launch_mode<MODE_GATEUP>(sp.mf, gu_s, 1, FMT_BF16, sp.tiles, ss, tr, ACT_BF16, "expert_gate_up_shared");
     if (err != hipSuccess) return err;
   }
   // (MXFP4 weights with bf16 activations read one h plane, so their down GEMM keeps the
@@ -1292,7 +1296,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   dn_s.out = y + pos * H;
   dn_s.E = 1; dn_s.S = 0; dn_s.limit = shared_limit;
   dn_s.dense = 1; dn_s.out_bf16 = 0; dn_s.bm_list = 16 * sp.mf; dn_s.group_major = sp.group_major;
-  return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, s, tr, ACT_BF16, "expert_down_shared");
+  return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, ss, tr, ACT_BF16, "expert_down_shared");
 }
 
 hipError_t launch_pack_mx(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t mats, int N, int Kd,

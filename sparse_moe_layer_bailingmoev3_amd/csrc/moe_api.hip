@@ -240,7 +240,8 @@ moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, i
 
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32_t* offsets,
                     const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
-                    hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false) {
+                    hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false, bool own_shared = false,
+                    hipStream_t shared_s = nullptr) {
   moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
                                   wfmt(c),
                                   c->hidden_size, c->moe_intermediate_size);
@@ -257,7 +258,8 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32
   hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),
                                         ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
                                         c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
-                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr, &ab);
+                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr, &ab, own_shared,
+                                        shared_s);
   if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   return MOE_OK;
 }
@@ -534,10 +536,54 @@ moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_sorte
 
 namespace {
 
+// The shared expert of a block-format layer runs on bf16 kernels of its own and reads x only,
+// so moe_forward gives it a second stream of the library's, forked from the caller's stream
+// at the start of the step and joined before the combine: it then runs beside the router, the
+// dispatch and the routed experts (all of which wait on their memory pipelines) instead of
+// after them.  One stream and two events per device, created on the device's first such
+// forward; the mutex is held from the fork to the join, so concurrent callers never reuse an
+// event before its wait is enqueued.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[MAX_DEVICES];
+
+// with g_side_mu held
+moe_status_t side_stream(SideStream** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond %d", dev, MAX_DEVICES);
+  SideStream& d = g_side[dev];
+  if (!d.s) {
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);  // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return hip_fail(e, "creating the shared expert's stream");
+    }
+    d = n;
+  }
+  *out = &d;
+  return MOE_OK;
+}
+
+moe_status_t route_dispatch_ffn(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                const float* expert_bias, const moe_expert_weights_t* weights, int32_t* idx,
+                                float* wts, int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv,
+                                void* y, const Layout& L, void* ws, hipStream_t s, moe::Tracer* tr,
+                                hipStream_t shared_s);
+
 moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
                           const float* expert_bias, const moe_expert_weights_t* weights, void* out,
                           int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
-                          size_t ws_bytes, void* stream, moe::Tracer* tr) {
+                          size_t ws_bytes, void* stream, moe::Tracer* tr, bool may_fork = true) {
   g_last_error.clear();
   moe_status_t st = validate_config(cfg, T);
   if (st != MOE_OK) return st;
@@ -561,6 +607,43 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
   int32_t* inv = (int32_t*)at(ws, L.inv_perm);
   void* y = at(ws, L.y);
   if (tr && tr->events && tr->cap > 0 && tr->events[0]) (void)hipEventRecord(tr->events[0], s);
+  // the shared expert of a block-format layer on the second stream (not when every kernel is
+  // followed by an event on the caller's stream: the trace times the kernels one by one)
+  // (bf16 layers keep the shared expert inside the routed launches: measured as launches of
+  // its own on the second stream, the 256-position tile kernels' prefill went 2.03 -> 2.05 ms
+  // and the skewed workload 2.64 -> 2.71 ms)
+  const bool fork = may_fork && cfg->num_shared_experts && wfmt(cfg) != moe::FMT_BF16 && !(tr && tr->events);
+  std::unique_lock<std::mutex> side_lock;
+  SideStream* side = nullptr;
+  if (fork) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mu);
+    if ((st = side_stream(&side)) != MOE_OK) return st;
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "forking the shared expert's stream");
+  }
+  st = route_dispatch_ffn(cfg, T, x, router_w, expert_bias, weights, idx, wts, counts, offsets, sorted_token, inv, y,
+                          L, ws, s, tr, fork ? side->s : s);
+  if (fork) {
+    // joined whatever happened above, so that no work of this step on the second stream can
+    // run after what the caller enqueues next
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+    side_lock.unlock();
+    if (st == MOE_OK && e != hipSuccess) return hip_fail(e, "joining the shared expert's stream");
+  }
+  if (st != MOE_OK) return st;
+  return do_combine(cfg, T, y, inv, wts, out, s, tr);
+}
+
+// router, dispatch and expert FFNs of one forward; the shared expert, where it has launches
+// of its own, goes to shared_s (the second stream or the caller's)
+moe_status_t route_dispatch_ffn(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
+                                const float* expert_bias, const moe_expert_weights_t* weights, int32_t* idx,
+                                float* wts, int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv,
+                                void* y, const Layout& L, void* ws, hipStream_t s, moe::Tracer* tr,
+                                hipStream_t shared_s) {
+  moe_status_t st;
   if (T <= moe::FUSED_DISPATCH_MAX_T && T * cfg->num_experts_per_tok <= moe::FUSED_DISPATCH_MAX_PAIRS &&
       cfg->num_experts <= moe::FUSED_DISPATCH_MAX_E) {
     // few tokens: the top-k kernel's last workgroup finishes the dispatch (one launch fewer)
@@ -580,8 +663,7 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
     if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
       return st;
   }
-  if ((st = do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true)) != MOE_OK) return st;
-  return do_combine(cfg, T, y, inv, wts, out, s, tr);
+  return do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true, true, shared_s);
 }
 
 }  // namespace
@@ -660,8 +742,9 @@ moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void*
     }
     ws = g_scratch_ptr[dev];
   }
+  // no second stream here: its first creation would allocate
   return forward_impl(cfg, T, x, router_w, expert_bias, weights, out, topk_idx_out, topk_w_out, expert_counts_out,
-                      ws, NOALLOC_SCRATCH_BYTES, stream, nullptr);
+                      ws, NOALLOC_SCRATCH_BYTES, stream, nullptr, false);
 }
 
 }  // extern "C"

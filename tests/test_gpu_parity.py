@@ -446,17 +446,24 @@ def test_determinism_tiny():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
-@pytest.mark.parametrize("T", [40, 700])
-def test_traced_and_timed_forwards_match_forward(T):
+@pytest.mark.parametrize("T,wfmt", [(40, "bf16"), (700, "bf16"), (2048, "bf16"), (40, "mxfp4"), (600, "mxfp8")])
+def test_traced_and_timed_forwards_match_forward(T, wfmt):
     """The profiling entry points compute the same layer, bit for bit; every kernel of the
     step can be timed by events bound to its dispatch, and an index past the last kernel is
-    an error (after the layer ran)."""
+    an error (after the layer ran).  With block-format experts, moe_forward and
+    moe_forward_timed run the shared expert on the library's second stream and
+    moe_forward_traced runs every kernel on the caller's: the same bits either way.  (T = 2048
+    puts the bf16 layer on the 256-position tile kernels.)"""
     import ctypes
     import torch
     import sparse_moe_layer_bailingmoev3_amd as moe
-    c = host_case(CONFIGS["tiny"], seed=11, T=T)
+    if wfmt == "bf16":
+        c = host_case(CONFIGS["tiny"], seed=11, T=T)
+    else:
+        c = host_case(CONFIGS["tiny"].with_(weight_format=wfmt), seed=11, T=T,
+                      experts=_tiny_block_experts(wfmt, 11))
     dev = DeviceCase(c)
-    say(f"[gpu] moe_forward / moe_forward_traced / moe_forward_timed, tiny T={T}")
+    say(f"[gpu] moe_forward / moe_forward_traced / moe_forward_timed, tiny T={T} {wfmt} experts")
     ref = dev.forward()[0].clone()
     hip = ctypes.CDLL("libamdhip64.so.7")
 
