@@ -22,7 +22,8 @@
  *
  * Conventions for every entry point
  *   - Pointers marked "device" are HIP device pointers the caller owns; the library
- *     keeps no pointer and no state after a call returns and allocates nothing.
+ *     keeps no pointer and no state after a call returns and allocates no device memory
+ *     (moe_forward's second stream, below, is the one object it keeps).
  *     Every device pointer must be 16-byte aligned.  Outputs must not alias inputs.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
  *     only enqueue work: they return before the GPU finishes, and a fault inside a
@@ -173,8 +174,10 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* top
  *   weights        host pointer to the device weight table above
  *   y_sorted       device fp32 [P,H]  (rows of the shared expert at T*K + t)
  * gate/up and down run on bf16 MFMA with fp32 accumulation.  The activation between them
- * is kept as two bf16 planes (hi = bf16(a), lo = bf16(a - hi)) and the down projection
- * multiplies both, so it keeps about 16 significand bits; MXFP4 weights are decoded
+ * is kept as two bf16 planes (hi = bf16(a), lo = bf16(a - hi)) by the few-token kernels
+ * (about 16 significand bits), as one fp16 plane by the 256-position tile kernels (11
+ * bits; down then runs on fp16 MFMA with its bf16 weights converted exactly), and as one
+ * bf16 plane for MXFP4 weights with bf16 activations; block-format weights are decoded
  * exactly to bf16 in registers. */
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
                             const int32_t* expert_offsets, const int32_t* sorted_token,
@@ -192,7 +195,12 @@ moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_sorte
  *   out                device bf16 [T,H]
  *   topk_idx_out, topk_w_out, expert_counts_out: optional device copies of the
  *   routing ([T,K] int32, [T,K] fp32, [E+1] int32); NULL to skip.
- * Equivalent to the four calls above in order, with the same results bit for bit. */
+ * Equivalent to the four calls above in order, with the same results bit for bit.
+ * With block-format experts and a shared expert, the shared expert's kernels (which read x
+ * only) run on a second stream of the library's, created once per device on its first such
+ * call (default priority), forked from `stream` before the router and joined back into
+ * `stream` before the combine: everything the call enqueues is still ordered after the
+ * work already on `stream` and before the work enqueued on it afterwards. */
 moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
                          const float* expert_bias, const moe_expert_weights_t* weights, void* out,
                          int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
