@@ -370,6 +370,14 @@ def measure_stack(shape, L, steps, warmup, hip):
             "tokens_per_s_per_layer": round(T / (ms / L * 1e-3), 1), "weights_GB": round(L * expert_bytes(shape) * E / 1e9, 1)}
 
 
+def y_value_bytes(shape) -> int:
+    """Bytes per value of the expert outputs y inside moe_forward: fp16 from the 256-position
+    tile kernels (bf16 experts, more than 12 tokens per expert on average; the tiny and full
+    hidden and intermediate sizes all fit those kernels), fp32 from the others."""
+    tiles = shape.weight_format == "bf16" and shape.T * shape.K / shape.E > 12
+    return 2 if tiles else 4
+
+
 def roofline(shape, r, workload=None, measured=None):
     """Roofline of the dominant kernel (the longer of gate/up and down), timed by two events
     bound to its dispatch in every step of the timed region.
@@ -377,7 +385,9 @@ def roofline(shape, r, workload=None, measured=None):
     Algorithmic bytes per launch (what the method has to move, once):
       expert_gate_up: (touched routed experts + shared) * 2*I*H weights in their storage
                       format + x [T,H] bf16 read + h [T*K + T, I] bf16 written;
-      expert_down:    (touched + shared) * H*I weights + h read + y [T*K + T, H] fp32 written.
+      expert_down:    (touched + shared) * H*I weights + h read + y [T*K + T, H] written, in
+                      fp16 where the forward runs the 256-position tile kernels (bf16 experts,
+                      more than 12 tokens per expert on average), else fp32.
     bf16 FLOPs per launch: 4*H*I per (token, expert) pair for gate/up, 2*H*I for down."""
     counts = r["counts"]
     E, H, I, K, T = shape.E, shape.H, shape.I, shape.K, shape.T
@@ -402,7 +412,7 @@ def roofline(shape, r, workload=None, measured=None):
         byts = touched * 2 * per_mat + S * 2 * sh_mat + x_b + h_b
         flops = 4.0 * H * I * pairs
     else:
-        byts = touched * per_mat + S * sh_mat + h_b + pairs * H * 4
+        byts = touched * per_mat + S * sh_mat + h_b + pairs * H * y_value_bytes(shape)
         flops = 2.0 * H * I * pairs
     ms = r["dom_ms"]
     gbs = byts / (ms * 1e-3) / 1e9

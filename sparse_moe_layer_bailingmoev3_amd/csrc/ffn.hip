@@ -1204,8 +1204,9 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
                              float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
                              bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab, bool own_shared,
-                             hipStream_t shared_s) {
+                             hipStream_t shared_s, bool y16) {
   hipError_t err = hipSuccess;
+  if (y16 && !p.tiles) return hipErrorInvalidValue;  // fp16 y only from the 256-position tile kernels
   const bool a8 = ab && ab->act == ACT_MXFP8;
   if (a8 && (p.tiles || w.fmt == FMT_BF16 || !ab->xq || !ab->xs || !ab->hq || !ab->hs)) return hipErrorInvalidValue;
   if (p.tiles) {
@@ -1216,7 +1217,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
       if (err != hipSuccess) return err;
     }
     return launch_expert_ffn_tiles(x, offsets, sorted_token, tile_prefix, p.max_tiles, w, T, H, I, E, S, limit,
-                                   shared_limit, h_hi, h_lo, y, s, tr);
+                                   shared_limit, h_hi, h_lo, y, s, tr, y16);
   }
   if (!tiles_ready) {
     launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix, tile_info_offset(E));

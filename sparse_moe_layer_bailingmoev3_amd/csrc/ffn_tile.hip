@@ -52,6 +52,7 @@ struct TileArgs {
   int rbw;                      // row blocks per workgroup
   int ngroups;                  // ceil(nrb / rbw)
   int interleave;               // 1: sub-tile t on XCD t mod 8; 0: contiguous item ranges per XCD
+  int y16;                      // down: y as fp16 [P,N] (saturated at +-65504) instead of fp32
   float limit, shared_limit;
 };
 
@@ -339,6 +340,12 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
               hv[r] = fminf(fmaxf(h, -65504.f), 65504.f);
             }
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_f16x2(hv[0], hv[1]), pack_f16x2(hv[2], hv[3])};
+          } else if (a.y16) {
+            // y in fp16 (11 significant bits), saturated like h
+            float yv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yv[r] = fminf(fmaxf(acc[0][f][tf][r], -65504.f), 65504.f);
+            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_f16x2(yv[0], yv[1]), pack_f16x2(yv[2], yv[3])};
           } else {
             *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][tf];
           }
@@ -443,7 +450,7 @@ bool ffn_tiles_supported(int H, int I) {
 hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                    const int32_t* tile_prefix, int64_t max_tiles, const FfnWeights& w, int T, int H,
                                    int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
-                                   uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr) {
+                                   uint16_t* h_lo, void* y, hipStream_t s, Tracer* tr, bool y16) {
   if (!ffn_tiles_supported(H, I)) return hipErrorInvalidValue;
   TileArgs gu{};
   gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
@@ -459,6 +466,7 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   gu.ngroups = (gu.nrb + gu.rbw - 1) / gu.rbw;
   gu.limit = limit; gu.shared_limit = shared_limit;
   gu.interleave = GU_INTERLEAVE;
+  gu.y16 = 0;
 
   TileArgs dn = gu;
   dn.act = h_hi; dn.sorted_token = nullptr;
@@ -466,6 +474,7 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   dn.out = y;
   dn.K = I; dn.N = H;
   dn.interleave = DN_INTERLEAVE;
+  dn.y16 = y16 ? 1 : 0;
   dn.nrb = H / (DN_RFR * 16); dn.rbw = std::min(dn.nrb, single ? 1 : DN_RBW);
   dn.ngroups = (dn.nrb + dn.rbw - 1) / dn.rbw;
 

@@ -241,7 +241,7 @@ moe_status_t do_dispatch(const moe_config_t* c, int64_t T, const int32_t* idx, i
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32_t* offsets,
                     const int32_t* sorted_token, const moe_expert_weights_t* w, void* y, const Layout& L, void* ws,
                     hipStream_t s, moe::Tracer* tr = nullptr, bool tiles_ready = false, bool own_shared = false,
-                    hipStream_t shared_s = nullptr) {
+                    hipStream_t shared_s = nullptr, bool y16 = false) {
   moe::FfnPlan p = moe::ffn_plan(T, c->num_experts_per_tok, c->num_experts, c->num_shared_experts,
                                   wfmt(c),
                                   c->hidden_size, c->moe_intermediate_size);
@@ -259,15 +259,15 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32
                                         ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
                                         c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
                                         (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr, &ab, own_shared,
-                                        shared_s);
+                                        shared_s, y16);
   if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   return MOE_OK;
 }
 
 moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* y, const int32_t* inv, const float* wts,
-                        void* out, hipStream_t s, moe::Tracer* tr = nullptr) {
-  hipError_t e = moe::launch_combine((const float*)y, inv, wts, (int)T, c->num_experts_per_tok, c->hidden_size,
-                                     c->num_shared_experts, (uint16_t*)out, s, tr);
+                        void* out, hipStream_t s, moe::Tracer* tr = nullptr, bool y16 = false) {
+  hipError_t e = moe::launch_combine(y, inv, wts, (int)T, c->num_experts_per_tok, c->hidden_size,
+                                     c->num_shared_experts, (uint16_t*)out, s, tr, y16);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;
 }
@@ -578,7 +578,7 @@ moe_status_t route_dispatch_ffn(const moe_config_t* cfg, int64_t T, const void* 
                                 const float* expert_bias, const moe_expert_weights_t* weights, int32_t* idx,
                                 float* wts, int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv,
                                 void* y, const Layout& L, void* ws, hipStream_t s, moe::Tracer* tr,
-                                hipStream_t shared_s);
+                                hipStream_t shared_s, bool y16);
 
 moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,
                           const float* expert_bias, const moe_expert_weights_t* weights, void* out,
@@ -622,8 +622,13 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "forking the shared expert's stream");
   }
+  // expert outputs y in fp16 where the 256-position tile kernels write them (bf16 experts
+  // from 13 tokens per expert up): half the down GEMM's writes and the combine's reads; the
+  // staged calls (moe_expert_ffn, moe_combine) keep their fp32 y_sorted
+  const bool y16 = moe::ffn_plan(T, cfg->num_experts_per_tok, cfg->num_experts, cfg->num_shared_experts, wfmt(cfg),
+                                 cfg->hidden_size, cfg->moe_intermediate_size).tiles;
   st = route_dispatch_ffn(cfg, T, x, router_w, expert_bias, weights, idx, wts, counts, offsets, sorted_token, inv, y,
-                          L, ws, s, tr, fork ? side->s : s);
+                          L, ws, s, tr, fork ? side->s : s, y16);
   if (fork) {
     // joined whatever happened above, so that no work of this step on the second stream can
     // run after what the caller enqueues next
@@ -633,7 +638,7 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
     if (st == MOE_OK && e != hipSuccess) return hip_fail(e, "joining the shared expert's stream");
   }
   if (st != MOE_OK) return st;
-  return do_combine(cfg, T, y, inv, wts, out, s, tr);
+  return do_combine(cfg, T, y, inv, wts, out, s, tr, y16);
 }
 
 // router, dispatch and expert FFNs of one forward; the shared expert, where it has launches
@@ -642,7 +647,7 @@ moe_status_t route_dispatch_ffn(const moe_config_t* cfg, int64_t T, const void* 
                                 const float* expert_bias, const moe_expert_weights_t* weights, int32_t* idx,
                                 float* wts, int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv,
                                 void* y, const Layout& L, void* ws, hipStream_t s, moe::Tracer* tr,
-                                hipStream_t shared_s) {
+                                hipStream_t shared_s, bool y16) {
   moe_status_t st;
   if (T <= moe::FUSED_DISPATCH_MAX_T && T * cfg->num_experts_per_tok <= moe::FUSED_DISPATCH_MAX_PAIRS &&
       cfg->num_experts <= moe::FUSED_DISPATCH_MAX_E) {
@@ -663,7 +668,7 @@ moe_status_t route_dispatch_ffn(const moe_config_t* cfg, int64_t T, const void* 
     if ((st = do_dispatch(cfg, T, idx, counts, offsets, sorted_token, inv, L, ws, s, tr, true, true)) != MOE_OK)
       return st;
   }
-  return do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true, true, shared_s);
+  return do_ffn(cfg, T, x, offsets, sorted_token, weights, y, L, ws, s, tr, true, true, shared_s, y16);
 }
 
 }  // namespace

@@ -147,7 +147,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr, const ActBufs* ab = nullptr, bool own_shared = false,
-                             hipStream_t shared_s = nullptr);
+                             hipStream_t shared_s = nullptr, bool y16 = false);
 // bf16 [rows, cols] -> MXFP8 codes [rows, cols] and e8m0 scales [rows, cols/32] (cols % 32 == 0)
 // row-major MXFP4 (fmt FMT_MXFP4) or MXFP8 arrays of `mats` matrices [N, Kd] -> the tiled order
 // of moe_pack_mxfp4 / moe_pack_mxfp8
@@ -167,12 +167,13 @@ hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uin
                                   const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
                                   uint16_t* h_lo, float* part, uint16_t* out, hipStream_t s);
 
-// 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles
+// 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles.
+// y16: y written as fp16 [P,H] (saturated at +-65504) instead of fp32
 bool ffn_tiles_supported(int H, int I);
 hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                    const int32_t* tile_prefix, int64_t max_tiles, const FfnWeights& w, int T, int H,
                                    int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
-                                   uint16_t* h_lo, float* y, hipStream_t s, Tracer* tr);
+                                   uint16_t* h_lo, void* y, hipStream_t s, Tracer* tr, bool y16 = false);
 
 // ---- dense FFN for few tokens (dense_ffn.hip) -----------------------------------
 // gate/up then down, each workgroup's waves splitting the reduction; h planes [T,I] in the
@@ -184,7 +185,9 @@ hipError_t launch_dense_ffn_small(const uint16_t* x, const uint16_t* gate, const
                                   hipStream_t s);
 
 // ---- combine -----------------------------------------------------------------
-hipError_t launch_combine(const float* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,
-                          int K, int H, int S, uint16_t* out, hipStream_t s, Tracer* tr = nullptr);
+// y16: y_sorted holds fp16 values (the tile kernels' y16 output) instead of fp32
+hipError_t launch_combine(const void* y_sorted, const int32_t* inv_perm, const float* topk_w, int T,
+                          int K, int H, int S, uint16_t* out, hipStream_t s, Tracer* tr = nullptr,
+                          bool y16 = false);
 
 }  // namespace moe
