@@ -371,11 +371,8 @@ def measure_stack(shape, L, steps, warmup, hip):
 
 
 def y_value_bytes(shape) -> int:
-    """Bytes per value of the expert outputs y inside moe_forward: fp16 from the 256-position
-    tile kernels (bf16 experts, more than 12 tokens per expert on average; the tiny and full
-    hidden and intermediate sizes all fit those kernels), fp32 from the others."""
-    tiles = shape.weight_format == "bf16" and shape.T * shape.K / shape.E > 12
-    return 2 if tiles else 4
+    """Bytes per value of the expert outputs y inside moe_forward: fp16 on every path."""
+    return 2
 
 
 def roofline(shape, r, workload=None, measured=None):
@@ -385,9 +382,7 @@ def roofline(shape, r, workload=None, measured=None):
     Algorithmic bytes per launch (what the method has to move, once):
       expert_gate_up: (touched routed experts + shared) * 2*I*H weights in their storage
                       format + x [T,H] bf16 read + h [T*K + T, I] bf16 written;
-      expert_down:    (touched + shared) * H*I weights + h read + y [T*K + T, H] written, in
-                      fp16 where the forward runs the 256-position tile kernels (bf16 experts,
-                      more than 12 tokens per expert on average), else fp32.
+      expert_down:    (touched + shared) * H*I weights + h read + y [T*K + T, H] fp16 written.
     bf16 FLOPs per launch: 4*H*I per (token, expert) pair for gate/up, 2*H*I for down."""
     counts = r["counts"]
     E, H, I, K, T = shape.E, shape.H, shape.I, shape.K, shape.T

@@ -62,6 +62,7 @@ struct FfnArgs {
                                 // shared expert of a block-format layer): tiles follow from T, no
                                 // dispatch arrays are read
   int out_bf16;                 // down writes bf16 out [T,N] (the dense FFN) instead of fp32 y
+  int y16;                      // down writes y as fp16 [P,N] (saturated at +-65504) instead of fp32
   int ksplit;                   // workgroups splitting the reduction (down of a dense FFN; else 1)
   float* part;                  // ksplit > 1: fp32 partial sums [ksplit,T,N], added in order later
   float limit, shared_limit;
@@ -412,6 +413,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
           } else if (a.out_bf16) {
             const floatx4 v = acc[0][f][mf];
             *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else if (a.y16) {
+            const floatx4 v = acc[0][f][mf];
+            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_f16x2_sat(v[0], v[1]), pack_f16x2_sat(v[2], v[3])};
           } else {
             *(floatx4*)((float*)a.out + obase + f * 16) = acc[0][f][mf];
           }
@@ -759,8 +763,14 @@ __device__ __forceinline__ void ffn_tile_a8(const FfnArgs& a, int e, int pos0, i
       } else {
         if (keep) {
 #pragma unroll
-          for (int f = 0; f < RF; ++f)
-            *(floatx4*)((float*)a.out + (size_t)(pos0 + j) * N + ncol0 + f * 16 + 4 * q) = acc[0][f][mf];
+          for (int f = 0; f < RF; ++f) {
+            const size_t o = (size_t)(pos0 + j) * N + ncol0 + f * 16 + 4 * q;
+            const floatx4 v = acc[0][f][mf];
+            if (a.y16)
+              *(u32x2*)((uint16_t*)a.out + o) = u32x2{pack_f16x2_sat(v[0], v[1]), pack_f16x2_sat(v[2], v[3])};
+            else
+              *(floatx4*)((float*)a.out + o) = v;
+          }
         }
       }
     }
@@ -1206,7 +1216,6 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab, bool own_shared,
                              hipStream_t shared_s, bool y16) {
   hipError_t err = hipSuccess;
-  if (y16 && !p.tiles) return hipErrorInvalidValue;  // fp16 y only from the 256-position tile kernels
   const bool a8 = ab && ab->act == ACT_MXFP8;
   if (a8 && (p.tiles || w.fmt == FMT_BF16 || !ab->xq || !ab->xs || !ab->hq || !ab->hs)) return hipErrorInvalidValue;
   if (p.tiles) {
@@ -1241,12 +1250,14 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
   gu.limit = limit; gu.shared_limit = shared_limit;
   gu.ksplit = 1;
+  gu.y16 = 0;
 
   FfnArgs dn = gu;
   dn.act = h_hi; dn.act_lo = h_lo; dn.sorted_token = nullptr; dn.out_lo = nullptr;
   dn.w0 = w.down; dn.w1 = nullptr; dn.s0 = w.down_scale; dn.s1 = nullptr;
   dn.sw0 = w.sh_down; dn.sw1 = nullptr; dn.out = y;
   dn.K = I; dn.N = H;
+  dn.y16 = y16 ? 1 : 0;
 
   gu.bm_list = dn.bm_list = p.bm;
   gu.group_major = dn.group_major = p.group_major ? 1 : 0;
@@ -1294,7 +1305,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   if (err != hipSuccess || !S) return err;
   dn_s.act = h_hi + pos * I; dn_s.act_lo = h_lo + pos * I;
   dn_s.w0 = w.sh_down; dn_s.s0 = nullptr;
-  dn_s.out = y + pos * H;
+  dn_s.out = y16 ? (void*)((uint16_t*)y + pos * H) : (void*)(y + pos * H);
   dn_s.E = 1; dn_s.S = 0; dn_s.limit = shared_limit;
   dn_s.dense = 1; dn_s.out_bf16 = 0; dn_s.bm_list = 16 * sp.mf; dn_s.group_major = sp.group_major;
   return launch_mode<MODE_DOWN>(sp.mf_down, dn_s, 1, FMT_BF16, sp.tiles, ss, tr, ACT_BF16, "expert_down_shared");

@@ -622,11 +622,9 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x, con
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "forking the shared expert's stream");
   }
-  // expert outputs y in fp16 where the 256-position tile kernels write them (bf16 experts
-  // from 13 tokens per expert up): half the down GEMM's writes and the combine's reads; the
-  // staged calls (moe_expert_ffn, moe_combine) keep their fp32 y_sorted
-  const bool y16 = moe::ffn_plan(T, cfg->num_experts_per_tok, cfg->num_experts, cfg->num_shared_experts, wfmt(cfg),
-                                 cfg->hidden_size, cfg->moe_intermediate_size).tiles;
+  // expert outputs y in fp16: half the down GEMM's writes and the combine's reads; the staged
+  // calls (moe_expert_ffn, moe_combine) keep their fp32 y_sorted
+  const bool y16 = true;
   st = route_dispatch_ffn(cfg, T, x, router_w, expert_bias, weights, idx, wts, counts, offsets, sorted_token, inv, y,
                           L, ws, s, tr, fork ? side->s : s, y16);
   if (fork) {

@@ -23,6 +23,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
+// two fp32 -> two fp16 (round to nearest even), saturated at +-65504 (finite inputs), low
+// half first
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
+  lo = fminf(fmaxf(lo, -65504.f), 65504.f);
+  hi = fminf(fmaxf(hi, -65504.f), 65504.f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand a: lane l holds row (l % 16) of the
 // 16-row tile, 8 consecutive k of the lane group (l / 16); operand b likewise for the

@@ -148,6 +148,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
                              uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr, const ActBufs* ab = nullptr, bool own_shared = false,
                              hipStream_t shared_s = nullptr, bool y16 = false);
+// (y16: y written as fp16 [P,H], saturated at +-65504, instead of fp32)
 // bf16 [rows, cols] -> MXFP8 codes [rows, cols] and e8m0 scales [rows, cols/32] (cols % 32 == 0)
 // row-major MXFP4 (fmt FMT_MXFP4) or MXFP8 arrays of `mats` matrices [N, Kd] -> the tiled order
 // of moe_pack_mxfp4 / moe_pack_mxfp8
