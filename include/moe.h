@@ -176,9 +176,10 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* top
  * gate/up and down run on bf16 MFMA with fp32 accumulation.  The activation between them
  * is kept as two bf16 planes (hi = bf16(a), lo = bf16(a - hi)) by the few-token kernels
  * (about 16 significand bits), as one fp16 plane by the 256-position tile kernels (11
- * bits; down then runs on fp16 MFMA with its bf16 weights converted exactly), and as one
- * bf16 plane for MXFP4 weights with bf16 activations; block-format weights are decoded
- * exactly to bf16 in registers. */
+ * bits; down then runs on fp16 MFMA with its bf16 weights converted exactly), as one
+ * bf16 plane for MXFP4 weights with bf16 activations and as one fp16 plane for MXFP8
+ * weights with bf16 activations (down decodes those weights to fp16 and runs on fp16
+ * MFMA); block-format weights are otherwise decoded exactly to bf16 in registers. */
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
                             const int32_t* expert_offsets, const int32_t* sorted_token,
                             const moe_expert_weights_t* weights, void* y_sorted, void* ws,

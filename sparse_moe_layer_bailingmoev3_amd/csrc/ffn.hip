@@ -108,6 +108,18 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t v0, uint32_t v1, float
   return o;
 }
 
+// The same 8 E4M3 codes times a power of two -> 8 fp16: exact while the products stay within
+// fp16's range (2^-24 .. 65504 in magnitude, i.e. block scales from 2^-15 to 2^7 for every
+// code; model weights sit far inside), smaller ones rounded to fp16's subnormal grid.
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t v0, uint32_t v1, float scale) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, scale, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, scale, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, scale, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, scale, true));
+  return o;
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);  // 2^(s-127)
 }
@@ -123,12 +135,18 @@ struct TStage {
   u32x4 t[NTP][CPT];
 };
 
-// bf16 planes of h the down GEMM reads: two (hi = bf16(h), lo = bf16(h - hi)) for bf16 and
-// MXFP8 expert weights, held to max|err| <= 2e-2 RMS; one for MXFP4 expert weights, held to
+// Planes of h the down GEMM reads: two bf16 (hi = bf16(h), lo = bf16(h - hi)) for bf16 expert
+// weights, held to max|err| <= 2e-2 RMS; one bf16 plane for MXFP4 expert weights, held to
 // 5e-2 RMS (the rounding of h to bf16 alone measured at most 2.5e-2 RMS, on the tiny layouts
-// with few, large expert sums), which halves the down GEMM's h bytes and MFMAs
+// with few, large expert sums); one fp16 plane (11 significant bits) for MXFP8 expert weights,
+// held to 2e-2 RMS, whose down GEMM decodes the weights to fp16 and runs on the fp16 MFMA.
+// One plane halves the down GEMM's h bytes and MFMAs.
 template <int MODE, int WF> struct HPlanes {
-  static constexpr int value = MODE == MODE_GATEUP || WF == FMT_MXFP4 ? 1 : 2;
+  static constexpr int value = MODE == MODE_GATEUP || WF != FMT_BF16 ? 1 : 2;
+};
+// h passes from gate/up to down in fp16 (MXFP8 expert weights)
+template <int WF> struct HFp16 {
+  static constexpr bool value = WF == FMT_MXFP8;
 };
 
 // One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
@@ -292,8 +310,16 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
       return fp4x8_to_bf16x8(st.w[m][f][0][s], e8m0_to_f32(st.sc[m][f]));
     } else {
       const float sc = e8m0_to_f32((st.sc[m][f] >> (8 * ((q >> 1) + 2 * (s >> 1)))) & 0xFFu);
-      return fp8x8_to_bf16x8(st.w[m][f][s >> 1][(2 * s) & 3], st.w[m][f][s >> 1][(2 * s + 1) & 3], sc);
+      if constexpr (MODE == MODE_DOWN && HFp16<WF>::value)
+        return fp8x8_to_f16x8(st.w[m][f][s >> 1][(2 * s) & 3], st.w[m][f][s >> 1][(2 * s + 1) & 3], sc);
+      else
+        return fp8x8_to_bf16x8(st.w[m][f][s >> 1][(2 * s) & 3], st.w[m][f][s >> 1][(2 * s + 1) & 3], sc);
     }
+  };
+  // the MFMA of this GEMM: fp16 for the down GEMM of MXFP8 weights (fp16 h), else bf16
+  auto mm = [](const u32x4& w, const u32x4& t, floatx4 c) -> floatx4 {
+    if constexpr (MODE == MODE_DOWN && HFp16<WF>::value) return mfma16_f16(w, t, c);
+    else return mfma16(w, t, c);
   };
   // the k offset, within a step, of the lane's sub-step s values (both operands)
   auto kcol = [&](int s) {
@@ -325,7 +351,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[m][f], tf, acc[m][f][mf]);
+            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mm(wf[m][f], tf, acc[m][f][mf]);
         }
       }
     }
@@ -376,7 +402,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mfma16(wf[s & 1][m][f], tf[s & 1][p][mf], acc[m][f][mf]);
+            for (int f = 0; f < RF; ++f) acc[m][f][mf] = mm(wf[s & 1][m][f], tf[s & 1][p][mf], acc[m][f][mf]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -405,9 +431,17 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
               hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
               lv[r] = h - hv[r];  // exact in fp32
             }
-            *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            if constexpr (HPlanes<MODE_DOWN, WF>::value == 2)
-              *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+            if constexpr (HFp16<WF>::value) {
+              float hf[4];  // h itself, rounded once to fp16
+#pragma unroll
+              for (int r = 0; r < 4; ++r) hf[r] = hv[r] + lv[r];
+              *(u32x2*)((uint16_t*)a.out + obase + f * 16) =
+                  u32x2{pack_f16x2_sat(hf[0], hf[1]), pack_f16x2_sat(hf[2], hf[3])};
+            } else {
+              *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+              if constexpr (HPlanes<MODE_DOWN, WF>::value == 2)
+                *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+            }
           } else if (a.ksplit > 1) {
             *(floatx4*)(a.part + ((size_t)ksp * a.T + pos0 + j) * N + ncol + f * 16) = acc[0][f][mf];
           } else if (a.out_bf16) {

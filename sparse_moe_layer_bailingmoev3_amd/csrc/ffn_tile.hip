@@ -87,10 +87,6 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& w) {
   return r;
 }
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ floatx4 mfma16_f16(const u32x4& a, const u32x4& b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
 
 // vmcnt wait with a compile-time count (other counters left alone)
 template <int N>

@@ -39,6 +39,12 @@ __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, floatx
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16x16x32 fp16 MFMA, fp32 accumulate; same operand and result layout as mfma16
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma16_f16(const u32x4& a, const u32x4& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Order-preserving map of an fp32 to uint32 (larger float -> larger integer).
 __device__ __forceinline__ uint32_t f32_ordered(float f) {
   uint32_t u = __float_as_uint(f);
