@@ -21,8 +21,9 @@
 //   * MFMA sub-step u takes k = 32u + 8q .. +7 for lane group q in both operands;
 //   * the SwiGLU activation h passes from gate/up to down as one fp16 plane (11 significant
 //     bits, where the few-token kernels keep two bf16 planes): the down GEMM converts each
-//     bf16 weight fragment to fp16 in registers (exact for these weights) and multiplies on
-//     the fp16 MFMA, at the bf16 rate, so h costs half the bytes and half the MFMAs.
+//     LDS stage of bf16 weights to fp16 in place once it has landed (each chunk by one lane,
+//     then a second barrier; exact for these weights) and multiplies on the fp16 MFMA, at
+//     the bf16 rate, so h costs half the bytes and half the MFMAs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -304,13 +305,25 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int tf = 0; tf < TPW; ++tf) acc[m][f][tf] = mfma16(wf[idx % (FPF + 1)], tv[0][tf][u], acc[m][f][tf]);
       } else {
-        // down: the bf16 weights as fp16 (exact from 2^-17 up), against the fp16 h
-        const u32x4 wh = bf16x8_to_f16x8(wf[idx % (FPF + 1)]);
+        // down: the weights, already converted to fp16 in the stage, against the fp16 h
 #pragma unroll
-        for (int tf = 0; tf < TPW; ++tf) acc[m][f][tf] = mfma16_f16(wh, tv[0][tf][u], acc[m][f][tf]);
+        for (int tf = 0; tf < TPW; ++tf) acc[m][f][tf] = mfma16_f16(wf[idx % (FPF + 1)], tv[0][tf][u], acc[m][f][tf]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // down: stage g's bf16 weights -> fp16 in place (exact from 2^-17 up to 65504, which holds
+  // bf16 model weights); the chunks of a stage are spread over all lanes of the workgroup
+  auto convert_stage = [&](int g) {
+    constexpr int CH = W_BYTES / 16 / (T_NW * 64);  // 16-byte chunks per lane
+    static_assert(CH * 16 * T_NW * 64 == W_BYTES, "a stage must split evenly over the lanes");
+    uint8_t* st = lds + (g % NSTAGE) * W_BYTES;
+    u32x4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = *(const u32x4*)(st + (c * T_NW * 64 + threadIdx.x) * 16);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) *(u32x4*)(st + (c * T_NW * 64 + threadIdx.x) * 16) = bf16x8_to_f16x8(v[c]);
   };
 
   auto epilogue = [&](int rbi) {
@@ -383,6 +396,12 @@ __global__ __launch_bounds__(T_NW * 64) void ffn_tile_kernel(TileArgs a) {
       wait_vmcnt<VM_WAIT>();
       lds_barrier();
       issue_w(g + D);
+      if constexpr (MODE == TM_DOWN) {
+        // the stage's bf16 weights become fp16 in place, each 16-byte chunk converted once by
+        // one lane (not by every wave that reads it), before any wave reads them
+        convert_stage(g);
+        lds_barrier();
+      }
       if (active) compute(g, tk[j]);
       issue_t(tk[j]);
       if (iss_live) ++isn;
