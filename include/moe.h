@@ -173,13 +173,12 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, int64_t T, const int32_t* top
  *   expert_offsets device int32 [E+2], sorted_token device int32 [P] (from moe_dispatch)
  *   weights        host pointer to the device weight table above
  *   y_sorted       device fp32 [P,H]  (rows of the shared expert at T*K + t)
- * gate/up and down run on bf16 MFMA with fp32 accumulation.  The activation between them
- * is kept as two bf16 planes (hi = bf16(a), lo = bf16(a - hi)) by the few-token kernels
- * (about 16 significand bits), as one fp16 plane by the 256-position tile kernels (11
- * bits; down then runs on fp16 MFMA with its bf16 weights converted exactly), as one
- * bf16 plane for MXFP4 weights with bf16 activations and as one fp16 plane for MXFP8
- * weights with bf16 activations (down decodes those weights to fp16 and runs on fp16
- * MFMA); block-format weights are otherwise decoded exactly to bf16 in registers. */
+ * gate/up runs on bf16 MFMA with fp32 accumulation.  The activation between the two
+ * products is kept as one fp16 plane (11 significant bits) for bf16 and MXFP8 expert
+ * weights, whose down product then runs on fp16 MFMA with the weights converted (bf16) or
+ * decoded (MXFP8) exactly to fp16; as one bf16 plane for MXFP4 weights with bf16
+ * activations; as MXFP8 with MXFP8 activations.  Block-format gate/up weights are decoded
+ * exactly to bf16 in registers. */
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
                             const int32_t* expert_offsets, const int32_t* sorted_token,
                             const moe_expert_weights_t* weights, void* y_sorted, void* ws,

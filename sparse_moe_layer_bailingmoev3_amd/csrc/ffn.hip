@@ -135,18 +135,16 @@ struct TStage {
   u32x4 t[NTP][CPT];
 };
 
-// Planes of h the down GEMM reads: two bf16 (hi = bf16(h), lo = bf16(h - hi)) for bf16 expert
-// weights, held to max|err| <= 2e-2 RMS; one bf16 plane for MXFP4 expert weights, held to
-// 5e-2 RMS (the rounding of h to bf16 alone measured at most 2.5e-2 RMS, on the tiny layouts
-// with few, large expert sums); one fp16 plane (11 significant bits) for MXFP8 expert weights,
-// held to 2e-2 RMS, whose down GEMM decodes the weights to fp16 and runs on the fp16 MFMA.
-// One plane halves the down GEMM's h bytes and MFMAs.
+// h passes from gate/up to down as one plane: fp16 (11 significant bits) for bf16 and MXFP8
+// expert weights, held to max|err| <= 2e-2 RMS, whose down GEMM converts the bf16 weights to
+// fp16 in registers (exact for model weights) or decodes the MXFP8 ones to fp16 and runs on
+// the fp16 MFMA; bf16 for MXFP4 expert weights, held to 5e-2 RMS (the rounding of h to bf16
+// alone measured at most 2.5e-2 RMS, on the tiny layouts with few, large expert sums).
 template <int MODE, int WF> struct HPlanes {
-  static constexpr int value = MODE == MODE_GATEUP || WF != FMT_BF16 ? 1 : 2;
+  static constexpr int value = 1;
 };
-// h passes from gate/up to down in fp16 (MXFP8 expert weights)
 template <int WF> struct HFp16 {
-  static constexpr bool value = WF == FMT_MXFP8;
+  static constexpr bool value = WF != FMT_MXFP4;
 };
 
 // One work unit.  D = prefetch distance: the loads of step s + D (weights and the token
@@ -156,7 +154,7 @@ template <int NW, int RF, int MF, int D, int MODE, int KS, int WF, bool PADDED>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int nrows, int rb0, int nrb_here,
                                          int ksp, uint16_t* lds) {
   constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
-  constexpr int NTP = HPlanes<MODE, WF>::value;  // token planes (down: h hi, and lo where kept)
+  constexpr int NTP = HPlanes<MODE, WF>::value;  // token planes (one: x for gate/up, h for down)
   constexpr int BM = MF * 16;
   constexpr int SUB = KS / 32;       // MFMA sub-steps per step
   constexpr int LROW = KS + 16;      // LDS row stride (bf16); the 32-byte pad measured fewest bank conflicts
@@ -339,6 +337,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         for (int f = 0; f < RF; ++f) {
           if constexpr (MX) {
             wf[m][f] = decode_mx(st, m, f, s);
+          } else if constexpr (MODE == MODE_DOWN && HFp16<WF>::value) {
+            wf[m][f] = bf16x8_to_f16x8(st.w[m][f][s]);
           } else {
             wf[m][f] = st.w[m][f][s];
           }
@@ -383,6 +383,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
         for (int f = 0; f < RF; ++f) {
           if constexpr (MX) {
             w[m][f] = decode_mx(st, m, f, s);
+          } else if constexpr (MODE == MODE_DOWN && HFp16<WF>::value) {
+            w[m][f] = bf16x8_to_f16x8(st.w[m][f][s]);
           } else {
             w[m][f] = st.w[m][f][s];
           }

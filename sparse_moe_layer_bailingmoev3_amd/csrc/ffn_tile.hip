@@ -76,18 +76,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
-// eight bf16 -> eight fp16: exact for magnitudes from 2^-17 (fp16 keeps the 8 significant bits
-// of bf16 down to there) up to 65504; smaller ones lose low bits toward zero (an absolute
-// error below 2^-24), larger ones (never bf16 model weights) become infinite
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& w) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
-                                                                     __uint_as_float(w[i] & 0xFFFF0000u)));
-  return r;
-}
-
 
 // vmcnt wait with a compile-time count (other counters left alone)
 template <int N>

@@ -45,6 +45,18 @@ __device__ __forceinline__ floatx4 mfma16_f16(const u32x4& a, const u32x4& b, fl
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// eight bf16 -> eight fp16: exact for magnitudes from 2^-17 (fp16 keeps the 8 significant bits
+// of bf16 down to there) up to 65504; smaller ones lose low bits toward zero (an absolute
+// error below 2^-24), larger ones (never bf16 model weights) become infinite
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                                                     __uint_as_float(w[i] & 0xFFFF0000u)));
+  return r;
+}
+
 // Order-preserving map of an fp32 to uint32 (larger float -> larger integer).
 __device__ __forceinline__ uint32_t f32_ordered(float f) {
   uint32_t u = __float_as_uint(f);
