@@ -141,7 +141,9 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.sorted_token = take(P * 4);
   L.inv_perm = take(T * K * 4);
   L.h_hi = take(P * I * 2);
-  L.h_lo = take(P * I * 2);
+  // h's second (lo) bf16 plane: only the dense FFN's few-token kernels still write one; every
+  // expert FFN kernel passes h as one plane
+  L.h_lo = take(T <= moe::DENSE_SMALL_MAX_T ? P * I * 2 : 0);
   L.y = take(P * H * 4);
   // MXFP8 activations: x and h as E4M3 codes and e8m0 scales (empty otherwise)
   const bool a8 = c->expert_act_format == MOE_ACT_MXFP8;
