@@ -308,7 +308,7 @@ moe_status_t moe_forward_timed(const moe_config_t* cfg, int64_t T, const void* x
  * which must be current).  The call allocates nothing.  T whose workspace
  * (moe_workspace_size) exceeds 64 MiB is rejected with MOE_ERR_WORKSPACE before anything is
  * enqueued: for the full-size layer (hidden 2560, 512 experts, intermediate 768) that is T
- * above about 500 tokens.  Every call on one GPU uses the same array and leaves its contents
+ * above about 970 tokens.  Every call on one GPU uses the same array and leaves its contents
  * behind (each call rewrites what it reads), so calls that overlap on one GPU -- on
  * different streams, or from different threads without ordering -- race. */
 moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x, const float* router_w,

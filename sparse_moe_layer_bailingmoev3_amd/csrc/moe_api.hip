@@ -115,7 +115,9 @@ struct Layout {
       xq, xs, hq, hs, total;
 };
 
-Layout layout(const moe_config_t* c, int64_t T) {
+// y_bytes: bytes per value of the expert outputs y in the workspace (2: moe_forward writes them
+// in fp16; 4: the dense FFN's one-expert path and its split partial sums)
+Layout layout(const moe_config_t* c, int64_t T, int y_bytes = 2) {
   const int64_t E = c->num_experts, K = c->num_experts_per_tok, H = c->hidden_size, I = c->moe_intermediate_size;
   const int64_t S = c->num_shared_experts;
   const int64_t P = T * K + T * S;
@@ -144,7 +146,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
   // h's second (lo) bf16 plane: only the dense FFN's few-token kernels still write one; every
   // expert FFN kernel passes h as one plane
   L.h_lo = take(T <= moe::DENSE_SMALL_MAX_T ? P * I * 2 : 0);
-  L.y = take(P * H * 4);
+  L.y = take(P * H * y_bytes);
   // MXFP8 activations: x and h as E4M3 codes and e8m0 scales (empty otherwise)
   const bool a8 = c->expert_act_format == MOE_ACT_MXFP8;
   L.xq = take(a8 ? T * H : 0);
@@ -155,8 +157,9 @@ Layout layout(const moe_config_t* c, int64_t T) {
   return L;
 }
 
-moe_status_t check_ws(const moe_config_t* c, int64_t T, const void* ws, size_t ws_bytes, Layout* out) {
-  Layout L = layout(c, T);
+moe_status_t check_ws(const moe_config_t* c, int64_t T, const void* ws, size_t ws_bytes, Layout* out,
+                      int y_bytes = 2) {
+  Layout L = layout(c, T, y_bytes);
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace must not be NULL");
   if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
   if (ws_bytes < L.total)
@@ -380,7 +383,7 @@ moe_config_t dense_config(int32_t H, int32_t I, float limit) {
 // the layer's workspace; with a split down reduction its partial sums start at the y region
 // (the last one) and may run past it
 size_t dense_ws_bytes(const moe_config_t* dc, int64_t T) {
-  const Layout L = layout(dc, T);
+  const Layout L = layout(dc, T, 4);
   const moe::FfnPlan p = moe::ffn_plan(T, 1, 1, 0, moe::FMT_BF16, dc->hidden_size, dc->moe_intermediate_size);
   if (p.ksplit_down <= 1) return L.total;
   return std::max(L.total, L.y + align256((size_t)p.ksplit_down * T * dc->hidden_size * 4));
@@ -426,7 +429,7 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
   w.down = down;
   if ((st = check_weights(&dc, &w)) != MOE_OK) return st;
   Layout L;
-  if ((st = check_ws(&dc, T, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if ((st = check_ws(&dc, T, ws, ws_bytes, &L, 4)) != MOE_OK) return st;
   if (ws_bytes < dense_ws_bytes(&dc, T))
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", ws_bytes, dense_ws_bytes(&dc, T),
                 (long long)T);
