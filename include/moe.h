@@ -66,7 +66,7 @@ typedef enum {
 } moe_weight_format_t;
 
 /* Activations of the routed experts' two matrix products.  MOE_ACT_BF16: x as given (bf16)
- * and h kept as two bf16 planes (about 16 significand bits).  MOE_ACT_MXFP8 (MXFP4 or MXFP8
+ * and h kept as one fp16 plane (11 significant bits; one bf16 plane for MXFP4 weights).  MOE_ACT_MXFP8 (MXFP4 or MXFP8
  * weights only): x and h rounded to MXFP8 -- E4M3 values with one e8m0 scale per 32
  * consecutive values along the reduction (OCP MX v1.0: scale = 2^(floor(log2 amax) - 8),
  * round to nearest even, saturate at 448) -- and multiplied by gfx950's scaled MFMA; the
@@ -215,8 +215,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
  * 4096, on the kernels of moe_expert_ffn with tiles computed from T and the output written by
  * the down GEMM (or, up to 512 tokens, by a last kernel adding the down GEMM's split
  * reduction in order); above, as a layer with a single routed expert that every token takes with
- * weight 1, on the kernels of moe_expert_ffn and moe_combine.  All paths round h the same way
- * (two bf16 planes) and sum in a fixed order, so they differ only by summation order.
+ * weight 1, on the kernels of moe_expert_ffn and moe_combine.  Up to 10 tokens h is kept as
+ * two bf16 planes (about 16 significand bits), above as one fp16 plane (11); every path sums
+ * in a fixed order.
  *   x device bf16 [T,H]; gate, up device bf16 [I,H]; down device bf16 [H,I]; out device
  *   bf16 [T,H]; ws device, 256-byte aligned, moe_dense_ffn_workspace_size bytes.
  *   H and I multiples of 128 (MOE_ERR_UNSUPPORTED otherwise); T = 0 is a no-op.

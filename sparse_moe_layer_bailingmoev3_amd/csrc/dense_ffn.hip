@@ -17,7 +17,8 @@
 //     1.6x slower (28 -> 47 us per call at T = 1): the memory system congests;
 //   * the NWK partial sums are added once through LDS, in wave order (deterministic), and the
 //     first wave runs the epilogue: SwiGLU, clamp and the two bf16 planes of h (hi = bf16(h),
-//     lo = bf16(h - hi), as in the expert FFN) after gate/up; after down, the bf16 output
+//     lo = bf16(h - hi); the expert FFN kernels keep one fp16 plane instead) after gate/up;
+//     after down, the bf16 output
 //     itself (a dense FFN has one slot per token with weight 1, so no combine is needed);
 //   * k permutation: lane group q of a 16-row operand owns the contiguous slice
 //     [q*KS/4, (q+1)*KS/4) of a step and MFMA sub-step s takes its s-th 8-value piece, the

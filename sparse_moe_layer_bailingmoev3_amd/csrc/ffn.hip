@@ -19,9 +19,10 @@
 //     scale block q of a step and sub-step s its s-th 8-value piece, for both operands (the
 //     same permutation of k on both sides leaves the dot products unchanged);
 //   * gate and up share the token operand; SwiGLU and the clamp run on the accumulators;
-//     the activation h is stored as two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
-//     and the down projection runs one MFMA per plane, so h keeps ~16 significand bits
-//     through the down GEMM; the down projection writes fp32 expert outputs;
+//     the activation h is stored as one plane: fp16 (11 significand bits) for bf16 and MXFP8
+//     weights, whose down GEMM converts (bf16) or decodes (MXFP8) its weights to fp16 and
+//     runs on the fp16 MFMA, bf16 for MXFP4 weights; the down projection writes fp32 expert
+//     outputs, or fp16 ones inside moe_forward;
 //   * MXFP4 weights (KS = 128: one 16-byte load = 32 codes = one scale block per lane) and
 //     MXFP8 weights (two 16-byte loads for the same 32 values) are decoded exactly to bf16 in
 //     registers by gfx950's scaled fp4 / fp8 -> bf16 conversions;
@@ -38,7 +39,6 @@ constexpr int MODE_GATEUP = 0, MODE_DOWN = 1;
 
 struct FfnArgs {
   const uint16_t* act;          // gate/up: x [T,K]; down: h hi plane [P,K]
-  const uint16_t* act_lo;       // down: h lo plane [P,K]
   const int32_t* sorted_token;  // gate/up: token of each sorted position
   const int32_t* offsets;       // [E+2]
   const int32_t* tile_prefix;   // [E+2] tiles of all experts before e
@@ -48,8 +48,7 @@ struct FfnArgs {
   const uint8_t* s1;            // MX scales of w1
   const void* sw0;              // shared expert gate or down
   const void* sw1;              // shared expert up
-  void* out;                    // gate/up: h hi plane bf16 [P,N]; down: y fp32 [P,N]
-  uint16_t* out_lo;             // gate/up: h lo plane bf16 [P,N]
+  void* out;                    // gate/up: h plane (fp16, or bf16 for MXFP4) [P,N]; down: y fp32 (fp16 with y16) [P,N]
   int T, E, S;
   int K;                        // reduction length
   int N;                        // output columns per expert
@@ -197,7 +196,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
       tsrc[0][i] = a.act + (size_t)((unsigned)tok < (unsigned)a.T ? tok : 0) * K + k0 + col;
     } else {
       tsrc[0][i] = a.act + (size_t)(pos0 + prow) * K + k0 + col;
-      if constexpr (NTP == 2) tsrc[NTP - 1][i] = a.act_lo + (size_t)(pos0 + prow) * K + k0 + col;
     }
     tvalid[i] = ok;
   }
@@ -424,26 +422,20 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int e, int pos0, int 
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
           if (MODE == MODE_GATEUP) {
-            float hv[4], lv[4];
+            float hv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float g = acc[0][f][mf][r], u = acc[NMAT - 1][f][mf][r];
               float h = g / (1.0f + __expf(-g)) * u;
               if (limit > 0.f) h = fminf(fmaxf(h, -limit), limit);
-              hv[r] = bf16_bits_to_f32(f32_to_bf16_bits(h));
-              lv[r] = h - hv[r];  // exact in fp32
+              hv[r] = h;
             }
-            if constexpr (HFp16<WF>::value) {
-              float hf[4];  // h itself, rounded once to fp16
-#pragma unroll
-              for (int r = 0; r < 4; ++r) hf[r] = hv[r] + lv[r];
+            // h rounded once: to fp16 (bf16 and MXFP8 weights) or to bf16 (MXFP4 weights)
+            if constexpr (HFp16<WF>::value)
               *(u32x2*)((uint16_t*)a.out + obase + f * 16) =
-                  u32x2{pack_f16x2_sat(hf[0], hf[1]), pack_f16x2_sat(hf[2], hf[3])};
-            } else {
+                  u32x2{pack_f16x2_sat(hv[0], hv[1]), pack_f16x2_sat(hv[2], hv[3])};
+            else
               *(u32x2*)((uint16_t*)a.out + obase + f * 16) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-              if constexpr (HPlanes<MODE_DOWN, WF>::value == 2)
-                *(u32x2*)(a.out_lo + obase + f * 16) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
-            }
           } else if (a.ksplit > 1) {
             *(floatx4*)(a.part + ((size_t)ksp * a.T + pos0 + j) * N + ncol + f * 16) = acc[0][f][mf];
           } else if (a.out_bf16) {
@@ -1063,9 +1055,9 @@ __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restri
 // Kernel configuration per (tile size, weight format, GEMM): NW waves, RF 16-row weight
 // blocks per wave (rows per workgroup and matrix NW*RF*16: 128, or 64 for the 16-token bf16
 // tiles of decode, whose smaller workgroups measured faster: gate/up 4 %, down 1.5 %), KS
-// values of k per step, D steps of loads in flight.  Otherwise the down GEMM, which reads two
-// h planes per token fragment, keeps two weight blocks per wave to halve its LDS reads per
-// MFMA.  16-token bf16 tiles (decode) take 256-value steps, two in flight, in 64-row
+// values of k per step, D steps of loads in flight.  Otherwise the down GEMM keeps two weight
+// blocks per wave to halve its LDS reads per MFMA (measured when it read two h planes per
+// token fragment).  16-token bf16 tiles (decode) take 256-value steps, two in flight, in 64-row
 // workgroups: each weight row then goes out in 512-byte runs (measured: decode gate/up 311 ->
 // 297 us, down 161 -> 159 us against 64-value steps); so does the gate/up of 32-token tiles
 // (T = 1024: 683 -> 655 us; their down GEMM measured slower that way).  The down GEMM of
@@ -1188,7 +1180,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
   p.topk = K;
   const double avg = (double)T * K / E;  // routed tokens per expert on average
   // tile list of 16*mf positions; gate/up runs whole tiles, down runs sub-tiles of 16*mf_down
-  // (measured: the down GEMM, which reads two h planes, is fastest with 64-token tiles at
+  // (measured when the down GEMM read two h planes: it is fastest with 64-token tiles at
   // two waves per SIMD; gate/up with 128, or 256 when experts average well above 128 tokens;
   // MXFP4 experts with up to 96 tokens on average take 64-token tiles: at 64 per expert,
   // gate/up 0.694 -> 0.731 ms but down 0.606 -> 0.548 ms)
@@ -1248,7 +1240,7 @@ FfnPlan ffn_plan(int64_t T, int K, int E, int S, int fmt, int H, int I) {
 
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                              int32_t* tile_prefix, const FfnWeights& w, int T, int H, int I, int E, int S,
-                             float limit, float shared_limit, uint16_t* h_hi, uint16_t* h_lo, float* y,
+                             float limit, float shared_limit, uint16_t* h, float* y,
                              bool tiles_ready, hipStream_t s, Tracer* tr, const ActBufs* ab, bool own_shared,
                              hipStream_t shared_s, bool y16) {
   hipError_t err = hipSuccess;
@@ -1262,7 +1254,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
       if (err != hipSuccess) return err;
     }
     return launch_expert_ffn_tiles(x, offsets, sorted_token, tile_prefix, p.max_tiles, w, T, H, I, E, S, limit,
-                                   shared_limit, h_hi, h_lo, y, s, tr, y16);
+                                   shared_limit, h, y, s, tr, y16);
   }
   if (!tiles_ready) {
     launch(tr, tile_prefix_kernel, dim3(1), dim3(64), s, offsets, E + S, p.bm, tile_prefix, tile_info_offset(E));
@@ -1282,14 +1274,14 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   FfnArgs gu{};
   gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
   gu.w0 = w.gate; gu.w1 = w.up; gu.s0 = w.gate_scale; gu.s1 = w.up_scale;
-  gu.sw0 = w.sh_gate; gu.sw1 = w.sh_up; gu.out = h_hi; gu.out_lo = h_lo;
+  gu.sw0 = w.sh_gate; gu.sw1 = w.sh_up; gu.out = h;
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
   gu.limit = limit; gu.shared_limit = shared_limit;
   gu.ksplit = 1;
   gu.y16 = 0;
 
   FfnArgs dn = gu;
-  dn.act = h_hi; dn.act_lo = h_lo; dn.sorted_token = nullptr; dn.out_lo = nullptr;
+  dn.act = h; dn.sorted_token = nullptr;
   dn.w0 = w.down; dn.w1 = nullptr; dn.s0 = w.down_scale; dn.s1 = nullptr;
   dn.sw0 = w.sh_down; dn.sw1 = nullptr; dn.out = y;
   dn.K = I; dn.N = H;
@@ -1327,7 +1319,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   if (S) {
     gu_s.act = x; gu_s.sorted_token = nullptr; gu_s.offsets = nullptr; gu_s.tile_prefix = nullptr;
     gu_s.w0 = w.sh_gate; gu_s.w1 = w.sh_up; gu_s.s0 = gu_s.s1 = nullptr;
-    gu_s.out = h_hi + pos * I; gu_s.out_lo = h_lo + pos * I;
+    gu_s.out = h + pos * I;
     gu_s.E = 1; gu_s.S = 0; gu_s.limit = shared_limit;
     gu_s.dense = 1; gu_s.bm_list = 16 * sp.mf; gu_s.group_major = sp.group_major;
     err = launch_mode<MODE_GATEUP>(sp.mf, gu_s, 1, FMT_BF16, sp.tiles, ss, tr, ACT_BF16, "expert_gate_up_shared");
@@ -1339,7 +1331,7 @@ hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t*
   // was fastest with two planes)
   err = launch_mode<MODE_DOWN>(p.mf_down, dn, p.rbw_down, w.fmt, p.max_tiles - sh_tiles, s, tr, act);
   if (err != hipSuccess || !S) return err;
-  dn_s.act = h_hi + pos * I; dn_s.act_lo = h_lo + pos * I;
+  dn_s.act = h + pos * I;
   dn_s.w0 = w.sh_down; dn_s.s0 = nullptr;
   dn_s.out = y16 ? (void*)((uint16_t*)y + pos * H) : (void*)(y + pos * H);
   dn_s.E = 1; dn_s.S = 0; dn_s.limit = shared_limit;
@@ -1375,12 +1367,12 @@ hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* 
 }
 
 hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
-                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
-                                  uint16_t* h_lo, float* part, uint16_t* out, hipStream_t s) {
+                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h,
+                                  float* part, uint16_t* out, hipStream_t s) {
   if (p.tiles) return hipErrorInvalidValue;  // the 256-position tile kernel reads the dispatch arrays
   if (p.ksplit_down > 1 && !part) return hipErrorInvalidValue;
   FfnArgs gu{};
-  gu.act = x; gu.w0 = gate; gu.w1 = up; gu.out = h_hi; gu.out_lo = h_lo;
+  gu.act = x; gu.w0 = gate; gu.w1 = up; gu.out = h;
   gu.T = T; gu.E = 1; gu.S = 0; gu.K = H; gu.N = I;
   gu.limit = limit;
   gu.bm_list = p.bm;
@@ -1388,7 +1380,7 @@ hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uin
   gu.dense = 1;
   gu.ksplit = 1;
   FfnArgs dn = gu;
-  dn.act = h_hi; dn.act_lo = h_lo; dn.out_lo = nullptr; dn.w0 = down; dn.w1 = nullptr; dn.out = out;
+  dn.act = h; dn.w0 = down; dn.w1 = nullptr; dn.out = out;
   dn.K = I; dn.N = H;
   dn.out_bf16 = 1;
   dn.ksplit = p.ksplit_down;

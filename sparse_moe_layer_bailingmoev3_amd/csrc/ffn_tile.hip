@@ -20,7 +20,7 @@
 //     keeps the MFMA fragment reads free of bank conflicts;
 //   * MFMA sub-step u takes k = 32u + 8q .. +7 for lane group q in both operands;
 //   * the SwiGLU activation h passes from gate/up to down as one fp16 plane (11 significant
-//     bits, where the few-token kernels keep two bf16 planes): the down GEMM converts each
+//     bits, as in the few-token kernels with bf16 weights): the down GEMM converts each
 //     LDS stage of bf16 weights to fp16 in place once it has landed (each chunk by one lane,
 //     then a second barrier; exact for these weights) and multiplies on the fp16 MFMA, at
 //     the bf16 rate, so h costs half the bytes and half the MFMAs.
@@ -46,7 +46,7 @@ struct TileArgs {
   const uint16_t* w1;           // routed up (gate/up)
   const uint16_t* sw0;          // shared expert gate or down
   const uint16_t* sw1;          // shared expert up
-  void* out;                    // gate/up: h fp16 [P,N]; down: y fp32 [P,N]
+  void* out;                    // gate/up: h fp16 [P,N]; down: y fp32 (fp16 with y16) [P,N]
   int T, E, S;
   int K, N;                     // reduction length, output columns per expert
   int nrb;                      // row blocks per expert (N / rows of one block)
@@ -452,14 +452,14 @@ bool ffn_tiles_supported(int H, int I) {
 // Launch gate/up and down with the 256-position tile list in tile_prefix.
 hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                    const int32_t* tile_prefix, int64_t max_tiles, const FfnWeights& w, int T, int H,
-                                   int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
-                                   uint16_t* h_lo, void* y, hipStream_t s, Tracer* tr, bool y16) {
+                                   int I, int E, int S, float limit, float shared_limit, uint16_t* h, void* y,
+                                   hipStream_t s, Tracer* tr, bool y16) {
   if (!ffn_tiles_supported(H, I)) return hipErrorInvalidValue;
   TileArgs gu{};
   gu.act = x; gu.sorted_token = sorted_token; gu.offsets = offsets; gu.tile_prefix = tile_prefix;
   gu.w0 = (const uint16_t*)w.gate; gu.w1 = (const uint16_t*)w.up;
   gu.sw0 = (const uint16_t*)w.sh_gate; gu.sw1 = (const uint16_t*)w.sh_up;
-  gu.out = h_hi;  // h as one fp16 plane (h_lo is not used by these kernels)
+  gu.out = h;  // h as one fp16 plane
   gu.T = T; gu.E = E; gu.S = S; gu.K = H; gu.N = I;
   // one weight set (a dense FFN): one row block per item, for twice the items (a single
   // expert has few token tiles to spread over the CUs)
@@ -472,7 +472,7 @@ hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, co
   gu.y16 = 0;
 
   TileArgs dn = gu;
-  dn.act = h_hi; dn.sorted_token = nullptr;
+  dn.act = h; dn.sorted_token = nullptr;
   dn.w0 = (const uint16_t*)w.down; dn.w1 = nullptr; dn.sw0 = (const uint16_t*)w.sh_down; dn.sw1 = nullptr;
   dn.out = y;
   dn.K = I; dn.N = H;

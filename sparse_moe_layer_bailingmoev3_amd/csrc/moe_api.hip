@@ -263,7 +263,7 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const int32
   hipError_t e = moe::launch_expert_ffn(p, (const uint16_t*)x, offsets, sorted_token, (int32_t*)at(ws, L.tile_prefix),
                                         ffn_weights(c, w), (int)T, c->hidden_size, c->moe_intermediate_size,
                                         c->num_experts, c->num_shared_experts, lim, slim, (uint16_t*)at(ws, L.h_hi),
-                                        (uint16_t*)at(ws, L.h_lo), (float*)y, tiles_ready, s, tr, &ab, own_shared,
+                                        (float*)y, tiles_ready, s, tr, &ab, own_shared,
                                         shared_s, y16);
   if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   return MOE_OK;
@@ -447,7 +447,7 @@ moe_status_t moe_dense_ffn(int32_t hidden_size, int32_t intermediate_size, float
     // the expert FFN kernels with the tiles computed from T (no dispatch, no combine)
     hipError_t e = moe::launch_dense_ffn_tiled(plan, (const uint16_t*)x, (const uint16_t*)gate, (const uint16_t*)up,
                                                (const uint16_t*)down, (int)T, hidden_size, intermediate_size,
-                                               dc.swiglu_limit, (uint16_t*)at(ws, L.h_hi), (uint16_t*)at(ws, L.h_lo),
+                                               dc.swiglu_limit, (uint16_t*)at(ws, L.h_hi),
                                                (float*)at(ws, L.y), (uint16_t*)out, s);
     if (e != hipSuccess) return hip_fail(e, "dense FFN launch");
     return MOE_OK;

@@ -134,7 +134,7 @@ struct SharedPlan {
 SharedPlan shared_plan(int64_t T);
 // MXFP8 activations of the routed experts (act == ACT_MXFP8): x rounded to MXFP8 (codes [T,H],
 // scales [T,H/32]) by a first kernel, h written by gate/up as MXFP8 (codes [P,I], scales
-// [P,I/32]); the shared expert keeps bf16 x and the two bf16 h planes
+// [P,I/32]); the shared expert keeps bf16 x and its fp16 h plane
 struct ActBufs {
   int act = ACT_BF16;
   uint8_t* xq = nullptr;
@@ -145,7 +145,7 @@ struct ActBufs {
 hipError_t launch_expert_ffn(const FfnPlan& p, const uint16_t* x, const int32_t* offsets,
                              const int32_t* sorted_token, int32_t* tile_prefix, const FfnWeights& w,
                              int T, int H, int I, int E, int S, float limit, float shared_limit,
-                             uint16_t* h_hi, uint16_t* h_lo, float* y, bool tiles_ready, hipStream_t s,
+                             uint16_t* h, float* y, bool tiles_ready, hipStream_t s,
                              Tracer* tr = nullptr, const ActBufs* ab = nullptr, bool own_shared = false,
                              hipStream_t shared_s = nullptr, bool y16 = false);
 // (y16: y written as fp16 [P,H], saturated at +-65504, instead of fp32)
@@ -165,16 +165,16 @@ hipError_t launch_mx8_quant(const uint16_t* x, int64_t rows, int cols, uint8_t* 
 constexpr int DENSE_MAX_KSPLIT = 16;
 constexpr int64_t DENSE_KSPLIT_MAX_T = 512;
 hipError_t launch_dense_ffn_tiled(const FfnPlan& p, const uint16_t* x, const uint16_t* gate, const uint16_t* up,
-                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h_hi,
-                                  uint16_t* h_lo, float* part, uint16_t* out, hipStream_t s);
+                                  const uint16_t* down, int T, int H, int I, float limit, uint16_t* h,
+                                  float* part, uint16_t* out, hipStream_t s);
 
 // 256-position tiles, bf16 weights (ffn_tile.hip); tile_prefix holds the 256-position tiles.
 // y16: y written as fp16 [P,H] (saturated at +-65504) instead of fp32
 bool ffn_tiles_supported(int H, int I);
 hipError_t launch_expert_ffn_tiles(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                    const int32_t* tile_prefix, int64_t max_tiles, const FfnWeights& w, int T, int H,
-                                   int I, int E, int S, float limit, float shared_limit, uint16_t* h_hi,
-                                   uint16_t* h_lo, void* y, hipStream_t s, Tracer* tr, bool y16 = false);
+                                   int I, int E, int S, float limit, float shared_limit, uint16_t* h,
+                                   void* y, hipStream_t s, Tracer* tr, bool y16 = false);
 
 // ---- dense FFN for few tokens (dense_ffn.hip) -----------------------------------
 // gate/up then down, each workgroup's waves splitting the reduction; h planes [T,I] in the
