@@ -446,6 +446,54 @@ def test_determinism_tiny():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
+def test_forwards_from_two_threads_block_format():
+    """With block-format experts moe_forward runs the shared expert on the library's second
+    stream, forked and joined under a mutex: two host threads that enqueue forwards at the same
+    time, each on its own stream with its own workspace, get the bits of forwards run one by
+    one."""
+    import threading
+    import torch
+    import sparse_moe_layer_bailingmoev3_amd as moe
+    devs = []
+    for seed, wfmt in ((41, "mxfp4"), (42, "mxfp8")):
+        c = host_case(CONFIGS["tiny"].with_(weight_format=wfmt), seed=seed, T=600,
+                      experts=_tiny_block_experts(wfmt, seed))
+        devs.append(DeviceCase(c))
+    say("[gpu] moe_forward from two host threads on two streams, tiny T=600 mxfp4 / mxfp8")
+    refs = [[t.clone() for t in d.forward()] for d in devs]
+    n = 12
+    outs = []
+    for d in devs:
+        s = d.c.shape
+        outs.append([(torch.empty((d.T, s.H), dtype=torch.bfloat16, device="cuda"),
+                      torch.empty((d.T, s.K), dtype=torch.int32, device="cuda"),
+                      torch.empty((d.T, s.K), dtype=torch.float32, device="cuda"),
+                      torch.empty((s.E + 1,), dtype=torch.int32, device="cuda")) for _ in range(n)])
+    streams = [torch.cuda.Stream() for _ in devs]  # default priority
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(i):
+        try:
+            d = devs[i]
+            for o in outs[i]:
+                moe.moe_forward(d.cfg, d.T, d.x, d.router_w, d.bias, d.weights, *o, d.ws, stream=streams[i])
+        except Exception as e:  # reported after the join
+            errors.append(e)
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(devs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for ref, runs in zip(refs, outs):
+        for o in runs:
+            for u, v in zip(ref, o):
+                assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                                   v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
 @pytest.mark.parametrize("T,wfmt", [(40, "bf16"), (700, "bf16"), (2048, "bf16"), (40, "mxfp4"), (600, "mxfp8")])
 def test_traced_and_timed_forwards_match_forward(T, wfmt):
     """The profiling entry points compute the same layer, bit for bit; every kernel of the
